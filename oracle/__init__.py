@@ -1,0 +1,174 @@
+"""fp64 CPU oracle for decode attention (ctypes binding of ``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code
+with the GPU library and never imports it.
+
+``attention`` evaluates softmax(Q K^T / sqrt(D)) V per output row in double
+precision, directly from the definition (see ``oracle.c`` for the readings
+taken: GQA head mapping, bottom-right causal alignment, empty rows).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+LIB_PATH = os.path.join(_HERE, "libmxfa_oracle.so")
+
+FP16, BF16 = 0, 1
+
+
+def compile_oracle(out_path: str = LIB_PATH, mutant: int = 0) -> str:
+    """Compile oracle.c with gcc (OpenMP, -O2, IEEE semantics kept)."""
+    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", f"-DMXO_MUTANT={int(mutant)}",
+           _SRC, "-o", out_path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+def build() -> None:
+    compile_oracle(LIB_PATH, 0)
+
+
+_lib_cache = {}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if path in _lib_cache:
+        return _lib_cache[path]
+    if not os.path.exists(path):
+        if path == LIB_PATH:
+            compile_oracle(path, 0)
+        else:
+            raise FileNotFoundError(path)
+    lib = ctypes.CDLL(path)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    ci = ctypes.c_int
+    lib.mxo_fp16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.mxo_fp16_to_f64.restype = ctypes.c_double
+    lib.mxo_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.mxo_bf16_to_f64.restype = ctypes.c_double
+    lib.mxo_attention.argtypes = [u16p, u16p, u16p, i32p] + [ci] * 8 + [f64p, f64p, ci]
+    lib.mxo_attention.restype = ci
+    lib.mxo_attention_rows.argtypes = ([u16p, u16p, u16p, i32p] + [ci] * 8 +
+                                       [i32p, ci, f64p, f64p, ci])
+    lib.mxo_attention_rows.restype = ci
+    lib.mxo_mutant_id.argtypes = []
+    lib.mxo_mutant_id.restype = ci
+    _lib_cache[path] = lib
+    return lib
+
+
+def _as_u16(x) -> np.ndarray:
+    """Bit patterns of a 16-bit float array (torch fp16/bf16 or numpy)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype in (torch.float16, torch.bfloat16):
+                x = x.view(torch.int16)
+            return x.numpy().view(np.uint16)
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(x)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    if a.dtype in (np.uint16, np.int16):
+        return a.view(np.uint16)
+    raise TypeError(f"unsupported array dtype {a.dtype}")
+
+
+def _dtype_code(x, dtype: Optional[str]) -> int:
+    if dtype is not None:
+        return {"fp16": FP16, "bf16": BF16}[dtype]
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return BF16 if x.dtype == torch.bfloat16 else FP16
+    except ImportError:  # pragma: no cover
+        pass
+    return FP16
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _seqlens(cache_seqlens, B: int):
+    if cache_seqlens is None:
+        return None
+    try:
+        import torch
+        if isinstance(cache_seqlens, torch.Tensor):
+            cache_seqlens = cache_seqlens.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    s = np.ascontiguousarray(np.asarray(cache_seqlens, dtype=np.int32))
+    assert s.shape == (B,)
+    return s
+
+
+def attention(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
+              dtype: Optional[str] = None, nthreads: int = 0,
+              lib_path: str = LIB_PATH) -> Tuple[np.ndarray, np.ndarray]:
+    """Return (out [B,qLen,Hq,D] float64, lse [B,Hq,qLen] float64)."""
+    qa, ka, va = _as_u16(q), _as_u16(k_cache), _as_u16(v_cache)
+    B, qLen, Hq, D = qa.shape
+    Bk, kv_cap, Hkv, Dk = ka.shape
+    assert Bk == B and Dk == D and va.shape == ka.shape
+    sl = _seqlens(cache_seqlens, B)
+    out = np.empty((B, qLen, Hq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, qLen), dtype=np.float64)
+    lib = load(lib_path)
+    rc = lib.mxo_attention(_ptr(qa, ctypes.c_uint16), _ptr(ka, ctypes.c_uint16),
+                           _ptr(va, ctypes.c_uint16),
+                           None if sl is None else _ptr(sl, ctypes.c_int32),
+                           B, Hq, Hkv, D, qLen, kv_cap, int(bool(causal)),
+                           _dtype_code(q, dtype), _ptr(out, ctypes.c_double),
+                           _ptr(lse, ctypes.c_double), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (rc={rc})")
+    return out, lse
+
+
+def attention_rows(q, k_cache, v_cache, rows: Sequence[Tuple[int, int, int]],
+                   cache_seqlens=None, causal: bool = False,
+                   dtype: Optional[str] = None, nthreads: int = 0,
+                   lib_path: str = LIB_PATH) -> Tuple[np.ndarray, np.ndarray]:
+    """Selected output rows (b, h, i): returns (out [n, D], lse [n])."""
+    qa, ka, va = _as_u16(q), _as_u16(k_cache), _as_u16(v_cache)
+    B, qLen, Hq, D = qa.shape
+    _, kv_cap, Hkv, _ = ka.shape
+    sl = _seqlens(cache_seqlens, B)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+    n = r.shape[0]
+    out = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    lib = load(lib_path)
+    rc = lib.mxo_attention_rows(_ptr(qa, ctypes.c_uint16), _ptr(ka, ctypes.c_uint16),
+                                _ptr(va, ctypes.c_uint16),
+                                None if sl is None else _ptr(sl, ctypes.c_int32),
+                                B, Hq, Hkv, D, qLen, kv_cap, int(bool(causal)),
+                                _dtype_code(q, dtype), _ptr(r, ctypes.c_int32), n,
+                                _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                                int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (rc={rc})")
+    return out, lse
+
+
+def decode16(bits: np.ndarray, dtype: str, lib_path: str = LIB_PATH) -> np.ndarray:
+    """Decode an array of 16-bit patterns to float64 with the oracle's decoder."""
+    lib = load(lib_path)
+    fn = lib.mxo_bf16_to_f64 if dtype == "bf16" else lib.mxo_fp16_to_f64
+    flat = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([fn(int(x)) for x in flat], dtype=np.float64).reshape(np.shape(bits))
