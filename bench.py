@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: achieved HBM GB/s and attention calls/s.
+
+One step = one split-KV decode attention call (split kernel + merge kernel)
+over one batch of seeded synthetic inputs already resident in HBM.  The
+default workload is the Qwen3-8B-shaped decode batch (B=64, qLen=1, Hq=32,
+Hkv=8, D=128, bf16, KV cache of 16384 with per-sequence lengths uniform in
+[1024, 16384], two K channels per head scaled x8).  Prints one JSON line.
+
+  value      algorithmic bytes per call / wall time per call (GB/s), where the
+             algorithmic bytes are Q + every visible K/V row once + out + lse
+             + cache_seqlens (nothing for scratch, the unread cache tail or
+             masked work);
+  roofline   the split kernel alone: its algorithmic bytes (K/V rows + Q) per
+             launch / its mean duration from HIP events recorded around it on
+             the stream it runs on, against the 8 TB/s HBM peak; traffic from
+             a committed rocprofv3 counter summary when it matches this build;
+  cpu_baseline  the fp64 CPU oracle timed on this host on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "qwen3_8b_decode"
+KERNEL_SOURCES = ["split_kv_decode_amd/csrc/split_valu.hip",
+                  "split_kv_decode_amd/csrc/device_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per split-kernel launch from the committed counter summary,
+    or None when there is none for this workload or the kernel changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_digest") != kernel_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the split-KV path shards by batch or kv head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import split_kv_decode_amd as mx
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    inp = wl.make_inputs(w)
+    lens = inp.lengths()
+    g = inp.to(dev)
+    print(f"# inputs {w.name} ({w.describe()}) generated in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+
+    dt = mx.MXFA_BF16 if w.dtype == "bf16" else mx.MXFA_FP16
+    need = mx.workspace_size(w.B, w.Hq, w.Hkv, w.D, w.qLen, w.kv_cap, w.causal, dt,
+                             args.num_splits)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(g.q)
+    lse = torch.empty((w.B, w.Hq, w.qLen), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        mx.fwd_kvcache(g.q, g.k_cache, g.v_cache, g.cache_seqlens, w.causal, out=out,
+                       lse=lse, num_splits=args.num_splits, workspace=ws,
+                       stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    plan = mx.last_plan().as_dict()
+
+    # whole calls, wall clock over exactly K steps
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    # split kernel alone: HIP events recorded around it on its stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:          # create the underlying HIP events
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for a, b in evs:
+        mx.set_timing_events(a.cuda_event, b.cuda_event)
+        call()
+    mx.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    split_ms = [a.elapsed_time(b) for a, b in evs]
+    split_ms_mean = float(np.mean(split_ms))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    alg_bytes = wl.algorithmic_bytes(w, lens)
+    kv = wl.kv_bytes(w, lens)
+    q_bytes = w.B * w.qLen * w.Hq * w.D * w.elt
+    split_bytes = kv + q_bytes
+    gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    split_gbs = split_bytes / (split_ms_mean * 1e-3) / 1e9
+    traffic = traffic_for(w.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = args.cpu_threads or len(os.sched_getaffinity(0))
+        tc = time.perf_counter()
+        oracle.attention(inp.q, inp.k_cache, inp.v_cache, inp.cache_seqlens, w.causal,
+                         w.dtype, nthreads=threads)
+        cpu_s = time.perf_counter() - tc
+        cpu = {"value": round(alg_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": (f"the whole {w.name} batch, one call ({cpu_s:.2f} s; "
+                          f"{alg_bytes / 1e9:.3f} GB algorithmic)")}
+
+    rec = {
+        "metric": "decode attention achieved HBM GB/s (% of peak) and attn-calls/s at B x KV len",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "qLen": w.qLen, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "D": w.D, "kv_cap": w.kv_cap, "sum_kv_len": int(sum(lens)),
+                   "causal": w.causal, "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "attn_calls_per_s": round(1e3 / ms_per_step, 1),
+        "plan": plan,
+        "roofline": {"bound": "hbm", "kernel": "split_kv_valu_kernel",
+                     "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "bytes_per_launch": split_bytes,
+                     "mean_launch_us": round(split_ms_mean * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * mxfa.h -- C ABI of the MI355X (gfx950) split-KV decode-attention library.
+ *
+ * One call computes FlashAttention-style forward attention for a few query
+ * tokens against a KV cache:
+ *
+ *     O = softmax(Q K^T / sqrt(D) [+ causal mask]) V          per query head,
+ *
+ * the formula of the interface section of "SmallQ FlashAttention for Ascend
+ * 910B" (scale 1/sqrt(headDim)), evaluated the FlashAttention way described
+ * in the ops-transformer articles (CSDN "FlashAttention in CANN
+ * ops-transformer", section on the FlashAttention idea and online softmax;
+ * mhpn.cn "ops-transformer source walk-through", section on tiling and
+ * online softmax): K/V are streamed tile by tile while a running maximum m,
+ * a running sum l and a rescaled output accumulator are kept on chip.  The
+ * KV sequence of every (batch, kv head) is cut into partitions that run in
+ * parallel ("M1 Split-KV decode" on the MXFlashAttn package page, use-case
+ * and verified-capability sections); a second kernel merges the partial
+ * (O, log-sum-exp) results.  Grouped-query attention: query head h reads kv
+ * head h / (Hq / Hkv) (GQA ratios as on the MXFlashAttn package page).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are contiguous, row-major, in device memory, all 16-bit tensors in
+ * the same dtype (mxfa_dtype):
+ *     q, out        [B, qLen, Hq, D]
+ *     k_cache,
+ *     v_cache       [B, kv_cap, Hkv, D]      kv_cap = cache capacity per sequence
+ *     cache_seqlens int32 [B]                valid length n_b of each sequence;
+ *                                            NULL means n_b = kv_cap for all b
+ *     lse           float32 [B, Hq, qLen]    natural log of sum_j exp(s_j), s_j
+ *                                            the scaled scores; may be NULL
+ * Values of cache_seqlens are read on the device and clamped to [0, kv_cap].
+ * Cache slots at or beyond n_b are never read.  With causal = 1 the mask is
+ * aligned to the bottom right: query row i (0 <= i < qLen) sees key j iff
+ * j <= i + n_b - qLen.  A row that sees no key gets O = 0 and lse = -inf.
+ * Arithmetic: 16-bit inputs, fp32 accumulation (as the SmallQ README's
+ * algorithm notes prescribe), output rounded to nearest-even.
+ *
+ * Supported: D in {64, 128} (the head dims verified on the MXFlashAttn
+ * package page); any Hq that is a multiple of Hkv; fp16 and bf16.  Other
+ * shapes return MXFA_ERR_UNSUPPORTED; nothing falls back silently.
+ *
+ * Ownership and threading: the caller owns every buffer.  The library keeps
+ * no pointer after a call returns.  Its only mutable state is the
+ * thread-local record of the last plan and a per-device cache of the CU
+ * count, so calls from several host threads are safe.
+ *
+ * Asynchrony: kernels are enqueued on `stream` (a hipStream_t; NULL = the
+ * null stream) and the call returns without synchronising.  The status
+ * covers argument checks and launch errors only; faults during execution
+ * surface at the caller's next synchronisation.
+ *
+ * Errors: all argument checks run before any HIP runtime call.  On any
+ * status other than MXFA_OK nothing has been enqueued and out / lse are
+ * untouched.
+ */
+#ifndef MXFA_H_
+#define MXFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MXFA_API __attribute__((visibility("default")))
+#else
+#define MXFA_API
+#endif
+
+typedef enum {
+    MXFA_OK = 0,
+    MXFA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad enum */
+    MXFA_ERR_UNSUPPORTED = 2,   /* valid request outside the supported shapes  */
+    MXFA_ERR_WORKSPACE = 3,     /* caller workspace missing or too small       */
+    MXFA_ERR_HIP = 4            /* HIP runtime error (allocation or launch)    */
+} mxfa_status;
+
+typedef enum { MXFA_FP16 = 0, MXFA_BF16 = 1 } mxfa_dtype;
+
+typedef enum {
+    MXFA_PATH_VALU = 0,         /* vector-ALU split kernel (few rows per kv head) */
+    MXFA_PATH_MFMA = 1          /* matrix-core split kernel (>= 8 rows per kv head) */
+} mxfa_path;
+
+/* How a call is carried out.  The analogue of the dispatch record the
+ * MXFlashAttn package exposes through get_last_dispatch_info (package page,
+ * "Python API" section): which kernel path ran and with what partitioning. */
+typedef struct {
+    int path;            /* mxfa_path */
+    int rows;            /* R = (Hq / Hkv) * qLen query rows per kv head */
+    int row_block;       /* query rows handled by one workgroup */
+    int num_splits;      /* S: KV partitions per (batch, kv head) at kv_cap */
+    int chunk;           /* tokens per partition (the last one may be shorter) */
+    int grid_x, grid_y, grid_z;  /* split-kernel grid (partitions, head/row blocks, batch) */
+    int combine;         /* 1 if the merge kernel runs (S > 1), else 0 */
+    int num_cus;         /* compute units the plan was made for */
+    size_t workspace_bytes;      /* device scratch the call needs (0 if S == 1) */
+} mxfa_plan_t;
+
+/* Split-KV decode attention, library-managed scratch.
+ * Partial results of the KV partitions go to a scratch buffer taken from
+ * the stream-ordered allocator (hipMallocAsync / hipFreeAsync on `stream`).
+ * Arguments as in the conventions above.  causal is 0 or 1; dtype is an
+ * mxfa_dtype.  Pointers q, k_cache, v_cache, out must be 16-byte aligned;
+ * lse and cache_seqlens 4-byte aligned.  B == 0 or qLen == 0 is a no-op.
+ * Returns MXFA_OK, or an error status as listed in mxfa_status. */
+MXFA_API mxfa_status mxfa_fwd_kvcache(const void *q, const void *k_cache,
+                                      const void *v_cache,
+                                      const int32_t *cache_seqlens, void *out,
+                                      float *lse, int B, int Hq, int Hkv,
+                                      int D, int qLen, int kv_cap, int causal,
+                                      int dtype, void *stream);
+
+/* Same computation with caller-provided scratch and an optional forced
+ * partition count.  num_splits = 0 lets the planner choose; a positive value
+ * asks for that many KV partitions per (batch, kv head) at kv_cap (clamped to
+ * [1, kv_cap]).  workspace must be 256-byte aligned and hold at least the
+ * number of bytes mxfa_workspace_size reports for the same arguments; it may
+ * be NULL when that number is 0.  The caller must not use the workspace for
+ * anything else until the work enqueued on `stream` has finished.
+ * Returns MXFA_ERR_WORKSPACE if the workspace is missing or too small. */
+MXFA_API mxfa_status mxfa_fwd_kvcache_ws(const void *q, const void *k_cache,
+                                         const void *v_cache,
+                                         const int32_t *cache_seqlens,
+                                         void *out, float *lse, int B, int Hq,
+                                         int Hkv, int D, int qLen, int kv_cap,
+                                         int causal, int dtype, int num_splits,
+                                         void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+/* Scratch bytes that mxfa_fwd_kvcache_ws needs for these arguments, written
+ * to *bytes.  The partitioning depends on the CU count of the current HIP
+ * device, so call it with the device current that will run the attention
+ * (the count is queried once per device and cached).  Returns the same
+ * validation statuses as the attention calls (checked before any HIP call),
+ * or MXFA_ERR_HIP if the device query fails. */
+MXFA_API mxfa_status mxfa_workspace_size(int B, int Hq, int Hkv, int D,
+                                         int qLen, int kv_cap, int causal,
+                                         int dtype, int num_splits,
+                                         size_t *bytes);
+
+/* The plan (path, partitioning, grid, scratch size) for a problem on a
+ * device with num_cus compute units (num_cus <= 0 means 256, an MI355X).
+ * Pure host code: makes no HIP runtime call, so it works without a GPU. */
+MXFA_API mxfa_status mxfa_plan(int B, int Hq, int Hkv, int D, int qLen,
+                               int kv_cap, int causal, int dtype,
+                               int num_splits, int num_cus, mxfa_plan_t *plan);
+
+/* The plan of the last successful attention call made by this host thread.
+ * Returns MXFA_ERR_INVALID_ARG if plan is NULL or no call has succeeded on
+ * this thread yet. */
+MXFA_API mxfa_status mxfa_last_plan(mxfa_plan_t *plan);
+
+/* Timing hook for benchmarks.  After this call, every attention call made by
+ * this host thread records the HIP event `before` on its stream immediately
+ * before the split-KV kernel is enqueued and `after` immediately after it, so
+ * hipEventElapsedTime(before, after) is that kernel's duration alone (the
+ * merge kernel is excluded).  The events (hipEvent_t) are created and owned
+ * by the caller and must stay valid while the hook is set.  Passing NULL for
+ * both turns the hook off; passing exactly one NULL returns
+ * MXFA_ERR_INVALID_ARG.  A failed event record makes the attention call
+ * return MXFA_ERR_HIP. */
+MXFA_API mxfa_status mxfa_set_timing_events(void *before, void *after);
+
+/* Static, human-readable text for a status value (never NULL). */
+MXFA_API const char *mxfa_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+MXFA_API int mxfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFA_H_ */

@@ -1,0 +1,320 @@
+// Host side of the C ABI declared in include/mxfa.h: argument checks (pure
+// host code, run before any HIP call), the partitioning planner, scratch
+// management and kernel launches.
+#include "../../include/mxfa.h"
+#include "launch.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+namespace {
+
+using namespace mxfa;
+
+constexpr int kVersion = 100;           // 0.1.0
+constexpr int kDefaultCUs = 256;        // MI355X
+constexpr int kMaxDevices = 64;
+constexpr int kMaxGridYZ = 65535;
+constexpr size_t kWsAlign = 256;
+
+// Problem-size checks only; pointers are checked separately.
+struct Problem {
+    int B, Hq, Hkv, D, qLen, kv_cap, causal, dtype;
+};
+
+thread_local mxfa_plan_t t_last_plan;
+thread_local bool t_has_last = false;
+thread_local hipEvent_t t_ev_before = nullptr;
+thread_local hipEvent_t t_ev_after = nullptr;
+
+std::atomic<int> g_cus[kMaxDevices];   // 0 = not yet queried
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t *out) {
+    return !__builtin_mul_overflow(a, b, out);
+}
+
+mxfa_status check_problem(const Problem &p) {
+    if (p.B < 0 || p.qLen < 0 || p.kv_cap < 0 || p.Hq <= 0 || p.Hkv <= 0 || p.D <= 0)
+        return MXFA_ERR_INVALID_ARG;
+    if (p.Hq % p.Hkv != 0) return MXFA_ERR_INVALID_ARG;
+    if (p.causal != 0 && p.causal != 1) return MXFA_ERR_INVALID_ARG;
+    if (p.dtype != MXFA_FP16 && p.dtype != MXFA_BF16) return MXFA_ERR_INVALID_ARG;
+    // byte sizes of every tensor must be representable
+    uint64_t x;
+    if (!mul_ok((uint64_t)p.B, (uint64_t)p.kv_cap, &x) || !mul_ok(x, (uint64_t)p.Hkv, &x) ||
+        !mul_ok(x, (uint64_t)p.D, &x) || !mul_ok(x, 2, &x) || x > (UINT64_C(1) << 62))
+        return MXFA_ERR_INVALID_ARG;
+    if (!mul_ok((uint64_t)p.B, (uint64_t)p.qLen, &x) || !mul_ok(x, (uint64_t)p.Hq, &x) ||
+        !mul_ok(x, (uint64_t)p.D, &x) || !mul_ok(x, 8, &x) || x > (UINT64_C(1) << 62))
+        return MXFA_ERR_INVALID_ARG;
+    if (p.D != 64 && p.D != 128) return MXFA_ERR_UNSUPPORTED;
+    if (p.B > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
+    return MXFA_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// k and v are never read when the cache has no capacity, so they may be NULL.
+mxfa_status check_pointers(const void *q, const void *k, const void *v,
+                           const int32_t *seqlens, const void *out, const float *lse,
+                           int kv_cap) {
+    if (!q || !out) return MXFA_ERR_INVALID_ARG;
+    if (kv_cap > 0 && (!k || !v)) return MXFA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return MXFA_ERR_INVALID_ARG;
+    if (seqlens && !aligned(seqlens, 4)) return MXFA_ERR_INVALID_ARG;
+    if (lse && !aligned(lse, 4)) return MXFA_ERR_INVALID_ARG;
+    return MXFA_OK;
+}
+
+int next_pow2_le8(int r) { return r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8; }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Partitioning.  Each (batch, kv head, row block) is one unit of work; the
+// KV axis of a unit is cut into S partitions of `chunk` tokens so that the
+// grid holds about 16 workgroups per CU at full length (several waves of
+// workgroups absorb the length spread of a ragged batch), while a partition
+// keeps at least kMinChunk tokens so the partial results stay a small
+// fraction of the K/V traffic.  The SmallQ README derives its KV block from
+// the on-chip buffer size; here the on-chip tile is fixed per kernel and the
+// planner only chooses the partition length.
+mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, mxfa_plan_t *plan) {
+    constexpr int kMinChunk = 256;
+    constexpr int kChunkAlign = 64;
+    constexpr int kTargetPerCU = 16;
+    mxfa_plan_t pl;
+    std::memset(&pl, 0, sizeof(pl));
+    if (num_cus <= 0) num_cus = kDefaultCUs;
+    const int G = p.Hq / p.Hkv;
+    const long long R = (long long)G * p.qLen;
+    if (R > INT32_MAX) return MXFA_ERR_UNSUPPORTED;
+    pl.path = MXFA_PATH_VALU;
+    pl.rows = (int)R;
+    pl.row_block = next_pow2_le8((int)R);
+    const int row_blocks = R > 0 ? ceil_div(R, pl.row_block) : 1;
+    if ((long long)p.Hkv * row_blocks > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
+    pl.num_cus = num_cus;
+
+    int S, chunk;
+    if (p.kv_cap == 0) {
+        S = 1;
+        chunk = 1;
+    } else if (num_splits > 0) {
+        S = num_splits > p.kv_cap ? p.kv_cap : num_splits;
+        chunk = ceil_div(p.kv_cap, S);
+        S = ceil_div(p.kv_cap, chunk);
+    } else {
+        const long long base = (long long)p.B * p.Hkv * row_blocks;
+        const long long target = (long long)num_cus * kTargetPerCU;
+        long long want = base > 0 ? (target + base - 1) / base : 1;
+        const long long smax = (p.kv_cap + kMinChunk - 1) / kMinChunk;
+        if (want > smax) want = smax;
+        if (want < 1) want = 1;
+        chunk = ceil_div(p.kv_cap, want);
+        chunk = ceil_div(chunk, kChunkAlign) * kChunkAlign;
+        S = ceil_div(p.kv_cap, chunk);
+    }
+    pl.num_splits = S;
+    pl.chunk = chunk;
+    pl.grid_x = S;
+    pl.grid_y = p.Hkv * row_blocks;
+    pl.grid_z = p.B;
+    pl.combine = S > 1 ? 1 : 0;
+    if (pl.combine) {
+        const size_t rows = (size_t)p.B * p.Hq * p.qLen * S;
+        const size_t o_bytes = (rows * p.D * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+        const size_t l_bytes = (rows * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+        pl.workspace_bytes = o_bytes + l_bytes;
+    }
+    *plan = pl;
+    return MXFA_OK;
+}
+
+mxfa_status device_cus(int *cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MXFA_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return MXFA_OK;
+        }
+    }
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        c <= 0)
+        return MXFA_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(c, std::memory_order_relaxed);
+    *cus = c;
+    return MXFA_OK;
+}
+
+mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seqlens,
+                void *out, float *lse, const Problem &p, const mxfa_plan_t &pl,
+                void *ws, hipStream_t stream) {
+    SplitArgs sa;
+    sa.q = q;
+    sa.k = k;
+    sa.v = v;
+    sa.seqlens = seqlens;
+    sa.out = out;
+    sa.lse = lse;
+    sa.ws_o = nullptr;
+    sa.ws_lse = nullptr;
+    if (pl.combine) {
+        const size_t rows = (size_t)p.B * p.Hq * p.qLen * pl.num_splits;
+        const size_t o_bytes = (rows * p.D * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+        sa.ws_o = (float *)ws;
+        sa.ws_lse = (float *)((char *)ws + o_bytes);
+    }
+    sa.B = p.B;
+    sa.Hq = p.Hq;
+    sa.Hkv = p.Hkv;
+    sa.qLen = p.qLen;
+    sa.kv_cap = p.kv_cap;
+    sa.G = p.Hq / p.Hkv;
+    sa.R = pl.rows;
+    sa.chunk = pl.chunk;
+    sa.S = pl.num_splits;
+    sa.qscale = (float)(1.4426950408889634 / std::sqrt((double)p.D));
+    const dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z);
+    if (t_ev_before && hipEventRecord(t_ev_before, stream) != hipSuccess) return MXFA_ERR_HIP;
+    if (launch_split_valu(sa, p.dtype, p.D, pl.row_block, p.causal, grid, stream) != hipSuccess)
+        return MXFA_ERR_HIP;
+    if (t_ev_after && hipEventRecord(t_ev_after, stream) != hipSuccess) return MXFA_ERR_HIP;
+    if (pl.combine) {
+        CombineArgs ca;
+        ca.ws_o = sa.ws_o;
+        ca.ws_lse = sa.ws_lse;
+        ca.seqlens = seqlens;
+        ca.out = out;
+        ca.lse = lse;
+        ca.B = p.B;
+        ca.Hq = p.Hq;
+        ca.qLen = p.qLen;
+        ca.kv_cap = p.kv_cap;
+        ca.chunk = pl.chunk;
+        ca.S = pl.num_splits;
+        if (launch_combine(ca, p.dtype, p.D, stream) != hipSuccess) return MXFA_ERR_HIP;
+    }
+    return MXFA_OK;
+}
+
+void record(const mxfa_plan_t &pl) {
+    t_last_plan = pl;
+    t_has_last = true;
+}
+
+}  // namespace
+
+extern "C" {
+
+MXFA_API mxfa_status mxfa_plan(int B, int Hq, int Hkv, int D, int qLen, int kv_cap,
+                               int causal, int dtype, int num_splits, int num_cus,
+                               mxfa_plan_t *plan) {
+    if (!plan || num_splits < 0) return MXFA_ERR_INVALID_ARG;
+    const Problem p{B, Hq, Hkv, D, qLen, kv_cap, causal, dtype};
+    mxfa_status st = check_problem(p);
+    if (st != MXFA_OK) return st;
+    return make_plan(p, num_splits, num_cus, plan);
+}
+
+MXFA_API mxfa_status mxfa_workspace_size(int B, int Hq, int Hkv, int D, int qLen, int kv_cap,
+                                         int causal, int dtype, int num_splits,
+                                         size_t *bytes) {
+    if (!bytes || num_splits < 0) return MXFA_ERR_INVALID_ARG;
+    const Problem p{B, Hq, Hkv, D, qLen, kv_cap, causal, dtype};
+    mxfa_status st = check_problem(p);
+    if (st != MXFA_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != MXFA_OK) return st;
+    mxfa_plan_t pl;
+    st = make_plan(p, num_splits, cus, &pl);
+    if (st != MXFA_OK) return st;
+    *bytes = (B == 0 || qLen == 0) ? 0 : pl.workspace_bytes;
+    return MXFA_OK;
+}
+
+MXFA_API mxfa_status mxfa_fwd_kvcache_ws(const void *q, const void *k_cache, const void *v_cache,
+                                         const int32_t *cache_seqlens, void *out, float *lse,
+                                         int B, int Hq, int Hkv, int D, int qLen, int kv_cap,
+                                         int causal, int dtype, int num_splits, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+    const Problem p{B, Hq, Hkv, D, qLen, kv_cap, causal, dtype};
+    mxfa_status st = check_problem(p);
+    if (st != MXFA_OK) return st;
+    if (num_splits < 0) return MXFA_ERR_INVALID_ARG;
+    if (B == 0 || qLen == 0) return MXFA_OK;       // nothing to compute
+    st = check_pointers(q, k_cache, v_cache, cache_seqlens, out, lse, kv_cap);
+    if (st != MXFA_OK) return st;
+    if (workspace && !aligned(workspace, kWsAlign)) return MXFA_ERR_INVALID_ARG;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != MXFA_OK) return st;
+    mxfa_plan_t pl;
+    st = make_plan(p, num_splits, cus, &pl);
+    if (st != MXFA_OK) return st;
+    if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
+        return MXFA_ERR_WORKSPACE;
+    st = run(q, k_cache, v_cache, cache_seqlens, out, lse, p, pl, workspace, (hipStream_t)stream);
+    if (st == MXFA_OK) record(pl);
+    return st;
+}
+
+MXFA_API mxfa_status mxfa_fwd_kvcache(const void *q, const void *k_cache, const void *v_cache,
+                                      const int32_t *cache_seqlens, void *out, float *lse,
+                                      int B, int Hq, int Hkv, int D, int qLen, int kv_cap,
+                                      int causal, int dtype, void *stream) {
+    const Problem p{B, Hq, Hkv, D, qLen, kv_cap, causal, dtype};
+    mxfa_status st = check_problem(p);
+    if (st != MXFA_OK) return st;
+    if (B == 0 || qLen == 0) return MXFA_OK;
+    st = check_pointers(q, k_cache, v_cache, cache_seqlens, out, lse, kv_cap);
+    if (st != MXFA_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != MXFA_OK) return st;
+    mxfa_plan_t pl;
+    st = make_plan(p, 0, cus, &pl);
+    if (st != MXFA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if (pl.workspace_bytes > 0 && hipMallocAsync(&ws, pl.workspace_bytes, s) != hipSuccess)
+        return MXFA_ERR_HIP;
+    st = run(q, k_cache, v_cache, cache_seqlens, out, lse, p, pl, ws, s);
+    if (ws && hipFreeAsync(ws, s) != hipSuccess && st == MXFA_OK) st = MXFA_ERR_HIP;
+    if (st == MXFA_OK) record(pl);
+    return st;
+}
+
+MXFA_API mxfa_status mxfa_last_plan(mxfa_plan_t *plan) {
+    if (!plan || !t_has_last) return MXFA_ERR_INVALID_ARG;
+    *plan = t_last_plan;
+    return MXFA_OK;
+}
+
+MXFA_API mxfa_status mxfa_set_timing_events(void *before, void *after) {
+    if ((before == nullptr) != (after == nullptr)) return MXFA_ERR_INVALID_ARG;
+    t_ev_before = (hipEvent_t)before;
+    t_ev_after = (hipEvent_t)after;
+    return MXFA_OK;
+}
+
+MXFA_API const char *mxfa_status_string(int status) {
+    switch (status) {
+    case MXFA_OK: return "MXFA_OK: success";
+    case MXFA_ERR_INVALID_ARG: return "MXFA_ERR_INVALID_ARG: invalid argument";
+    case MXFA_ERR_UNSUPPORTED: return "MXFA_ERR_UNSUPPORTED: unsupported shape (D must be 64 or 128)";
+    case MXFA_ERR_WORKSPACE: return "MXFA_ERR_WORKSPACE: workspace missing or too small";
+    case MXFA_ERR_HIP: return "MXFA_ERR_HIP: HIP runtime error";
+    default: return "unknown mxfa status";
+    }
+}
+
+MXFA_API int mxfa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+"""ctypes binding of libmxfa.so (include/mxfa.h).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current HIP stream.
+If the library has not been built this module raises on first use; there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxfa.so")
+
+MXFA_OK, MXFA_ERR_INVALID_ARG, MXFA_ERR_UNSUPPORTED, MXFA_ERR_WORKSPACE, MXFA_ERR_HIP = range(5)
+MXFA_FP16, MXFA_BF16 = 0, 1
+PATH_NAMES = {0: "valu", 1: "mfma"}
+
+# every symbol include/mxfa.h declares
+EXPORTS = ("mxfa_fwd_kvcache", "mxfa_fwd_kvcache_ws", "mxfa_workspace_size",
+           "mxfa_plan", "mxfa_last_plan", "mxfa_set_timing_events",
+           "mxfa_status_string", "mxfa_version")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("rows", ctypes.c_int),
+                ("row_block", ctypes.c_int), ("num_splits", ctypes.c_int),
+                ("chunk", ctypes.c_int), ("grid_x", ctypes.c_int),
+                ("grid_y", ctypes.c_int), ("grid_z", ctypes.c_int),
+                ("combine", ctypes.c_int), ("num_cus", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self) -> dict:
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["path"] = PATH_NAMES.get(self.path, str(self.path))
+        return d
+
+
+class MxfaError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = status_string(status)
+        super().__init__(f"{what}: {msg}" if what else msg)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxfa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python split_kv_decode_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.mxfa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 8 + [vp]
+    L.mxfa_fwd_kvcache.restype = ci
+    L.mxfa_fwd_kvcache_ws.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 9 + [vp, sz, vp]
+    L.mxfa_fwd_kvcache_ws.restype = ci
+    L.mxfa_workspace_size.argtypes = [ci] * 9 + [ctypes.POINTER(sz)]
+    L.mxfa_workspace_size.restype = ci
+    L.mxfa_plan.argtypes = [ci] * 10 + [ctypes.POINTER(Plan)]
+    L.mxfa_plan.restype = ci
+    L.mxfa_last_plan.argtypes = [ctypes.POINTER(Plan)]
+    L.mxfa_last_plan.restype = ci
+    L.mxfa_set_timing_events.argtypes = [vp, vp]
+    L.mxfa_set_timing_events.restype = ci
+    L.mxfa_status_string.argtypes = [ci]
+    L.mxfa_status_string.restype = ctypes.c_char_p
+    L.mxfa_version.argtypes = []
+    L.mxfa_version.restype = ci
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().mxfa_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return lib().mxfa_version()
+
+
+def plan(B, Hq, Hkv, D, qLen, kv_cap, causal=False, dtype=MXFA_FP16, num_splits=0,
+         num_cus=0) -> Plan:
+    p = Plan()
+    st = lib().mxfa_plan(B, Hq, Hkv, D, qLen, kv_cap, int(causal), int(dtype),
+                         int(num_splits), int(num_cus), ctypes.byref(p))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_plan")
+    return p
+
+
+def last_plan() -> Plan:
+    p = Plan()
+    st = lib().mxfa_last_plan(ctypes.byref(p))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_last_plan")
+    return p
+
+
+def set_timing_events(before=None, after=None) -> None:
+    """Record raw HIP events (handles as ints, e.g. torch.cuda.Event.cuda_event)
+    around the split kernel of every later call on this thread; None, None
+    turns it off."""
+    vp = lambda e: None if e is None else ctypes.c_void_p(int(e))
+    st = lib().mxfa_set_timing_events(vp(before), vp(after))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_set_timing_events")
+
+
+def workspace_size(B, Hq, Hkv, D, qLen, kv_cap, causal=False, dtype=MXFA_FP16,
+                   num_splits=0) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().mxfa_workspace_size(B, Hq, Hkv, D, qLen, kv_cap, int(causal), int(dtype),
+                                   int(num_splits), ctypes.byref(n))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_workspace_size")
+    return n.value
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return MXFA_FP16
+    if t.dtype == torch.bfloat16:
+        return MXFA_BF16
+    raise TypeError(f"q must be float16 or bfloat16, got {t.dtype}")
+
+
+def fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
+                out=None, lse=None, return_lse: bool = True, num_splits: int = 0,
+                workspace=None, stream=None) -> Tuple[object, Optional[object]]:
+    """Decode attention on the current HIP stream; returns (out, lse).
+
+    q [B, qLen, Hq, D]; k_cache, v_cache [B, kv_cap, Hkv, D] (fp16 or bf16,
+    contiguous, on one GPU); cache_seqlens int32 [B] or None.  With
+    num_splits > 0 or an explicit workspace (a uint8 tensor), the
+    caller-workspace entry point is used; otherwise the library allocates
+    its scratch on the stream.
+    """
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, qLen, Hq, D = q.shape
+    Bk, kv_cap, Hkv, Dk = k_cache.shape
+    if Bk != B or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache must be [B, kv_cap, Hkv, D] matching q")
+    dt = _dtype_code(q)
+    if cache_seqlens is not None:
+        if (cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda
+                or tuple(cache_seqlens.shape) != (B,) or not cache_seqlens.is_contiguous()):
+            raise ValueError("cache_seqlens must be a contiguous int32 GPU tensor of shape [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, qLen), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, qLen)
+                              or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, qLen]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    args = (ptr(q), ptr(k_cache), ptr(v_cache), ptr(cache_seqlens), ptr(out), ptr(lse),
+            B, Hq, Hkv, D, qLen, kv_cap, int(bool(causal)), dt)
+    with torch.cuda.device(q.device):
+        if workspace is None and num_splits == 0:
+            st = lib().mxfa_fwd_kvcache(*args, ctypes.c_void_p(stream))
+        else:
+            if workspace is None:
+                need = workspace_size(B, Hq, Hkv, D, qLen, kv_cap, causal, dt, num_splits)
+                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+            st = lib().mxfa_fwd_kvcache_ws(*args, int(num_splits), ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           ctypes.c_void_p(stream))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_fwd_kvcache")
+    return out, lse

@@ -1,0 +1,174 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before making any HIP call (so every
+error path below runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import split_kv_decode_amd as m
+from split_kv_decode_amd import mxfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfa.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MXFA_API\s+[\w\s\*]+?\b(mxfa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = m.lib()
+    declared = header_functions()
+    assert declared == sorted(mxfa.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_only_declared_symbols_are_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", mxfa.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines()
+                       if " T " in l and l.split()[-1].startswith("mxfa_")})
+    assert exported == header_functions()
+
+
+def test_status_strings_and_version():
+    for s in range(5):
+        assert m.status_string(s).startswith("MXFA_")
+    assert "unknown" in m.status_string(99)
+    assert m.version() >= 100
+
+
+def test_last_plan_before_any_call_is_an_error():
+    import threading
+    res = {}
+
+    def worker():
+        try:
+            m.last_plan()
+        except m.MxfaError as e:
+            res["status"] = e.status
+    t = threading.Thread(target=worker)
+    t.start()
+    t.join()
+    assert res["status"] == mxfa.MXFA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- validation
+
+def _call(**kw):
+    """mxfa_fwd_kvcache with fake (never dereferenced) aligned pointers."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, sl=0, out=0x40000, lse=0x50000,
+             B=2, Hq=8, Hkv=2, D=128, qLen=1, cap=64, causal=0, dtype=0)
+    a.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    return m.lib().mxfa_fwd_kvcache(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["sl"]),
+                                    vp(a["out"]), vp(a["lse"]), a["B"], a["Hq"], a["Hkv"],
+                                    a["D"], a["qLen"], a["cap"], a["causal"], a["dtype"], None)
+
+
+def _call_ws(num_splits=0, ws=None, ws_bytes=0, **kw):
+    a = dict(q=0x10000, k=0x20000, v=0x30000, sl=0, out=0x40000, lse=0x50000,
+             B=2, Hq=8, Hkv=2, D=128, qLen=1, cap=64, causal=0, dtype=0)
+    a.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    return m.lib().mxfa_fwd_kvcache_ws(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["sl"]),
+                                       vp(a["out"]), vp(a["lse"]), a["B"], a["Hq"], a["Hkv"],
+                                       a["D"], a["qLen"], a["cap"], a["causal"], a["dtype"],
+                                       num_splits, vp(ws), ws_bytes, None)
+
+
+INV, UNS = mxfa.MXFA_ERR_INVALID_ARG, mxfa.MXFA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), INV), (dict(k=0), INV), (dict(v=0), INV), (dict(out=0), INV),
+    (dict(q=0x10008), INV), (dict(k=0x20004), INV), (dict(v=0x30002), INV),
+    (dict(out=0x40001), INV), (dict(lse=0x50002), INV), (dict(sl=0x60001), INV),
+    (dict(B=-1), INV), (dict(qLen=-2), INV), (dict(cap=-1), INV), (dict(Hq=0), INV),
+    (dict(Hkv=0), INV), (dict(D=0), INV), (dict(Hq=6, Hkv=4), INV),
+    (dict(causal=2), INV), (dict(causal=-1), INV), (dict(dtype=2), INV), (dict(dtype=-1), INV),
+    (dict(B=2**30, cap=2**30), INV),                       # byte size overflow
+    (dict(D=96), UNS), (dict(D=256), UNS), (dict(D=32), UNS), (dict(B=70000), UNS),
+])
+def test_invalid_arguments_rejected_before_any_hip_call(kw, status):
+    assert _call(**kw) == status
+    assert _call_ws(**kw) == status
+
+
+def test_empty_problem_is_a_no_op():
+    assert _call(B=0) == mxfa.MXFA_OK
+    assert _call(qLen=0) == mxfa.MXFA_OK
+    assert _call(B=0, q=0, k=0, v=0, out=0) == mxfa.MXFA_OK
+    assert _call_ws(qLen=0) == mxfa.MXFA_OK
+
+
+def test_ws_rejects_negative_splits_and_misaligned_workspace():
+    assert _call_ws(num_splits=-1) == INV
+    assert _call_ws(ws=0x70010, ws_bytes=1 << 20) == INV
+
+
+def test_workspace_size_argument_checks():
+    n = ctypes.c_size_t()
+    L = m.lib()
+    assert L.mxfa_workspace_size(1, 8, 2, 128, 1, 64, 0, 0, 0, None) == INV
+    assert L.mxfa_workspace_size(1, 8, 3, 128, 1, 64, 0, 0, 0, ctypes.byref(n)) == INV
+    assert L.mxfa_workspace_size(1, 8, 2, 80, 1, 64, 0, 0, 0, ctypes.byref(n)) == UNS
+    assert L.mxfa_workspace_size(1, 8, 2, 128, 1, 64, 0, 0, -3, ctypes.byref(n)) == INV
+
+
+# ---------------------------------------------------------------- planner
+
+SHAPES = [
+    # B, Hq, Hkv, D, qLen, cap, causal, dtype
+    (1, 8, 2, 64, 32, 128, 1, 0),
+    (1, 32, 32, 128, 1, 1023, 0, 0),
+    (1, 32, 32, 128, 8, 4096, 0, 0),
+    (64, 32, 8, 128, 1, 16384, 0, 1),
+    (16, 32, 8, 128, 1, 16384, 0, 0),
+    (4, 64, 8, 128, 8, 32768, 1, 1),
+    (3, 10, 2, 64, 3, 77, 1, 1),
+    (2, 4, 4, 128, 1, 0, 0, 0),
+    (1, 1, 1, 64, 1, 1, 0, 0),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 3, 7, 1000])
+def test_plan_covers_the_cache_exactly(shape, num_splits):
+    B, Hq, Hkv, D, qLen, cap, causal, dt = shape
+    p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits)
+    S, C = p.num_splits, p.chunk
+    assert S >= 1 and C >= 1
+    if cap > 0:
+        assert (S - 1) * C < cap <= S * C          # every partition non-empty at kv_cap
+        if num_splits:
+            assert S <= min(num_splits, cap)
+    assert p.rows == (Hq // Hkv) * qLen
+    assert p.row_block in (1, 2, 4, 8) and p.row_block >= min(p.rows, 8)
+    assert p.grid_x == S and p.grid_z == B
+    assert p.grid_y == Hkv * -(-p.rows // p.row_block)
+    assert p.combine == (1 if S > 1 else 0)
+    if S > 1:
+        assert p.workspace_bytes >= B * Hq * qLen * S * (D + 1) * 4
+    else:
+        assert p.workspace_bytes == 0
+
+
+def test_plan_fills_the_chip_at_low_batch():
+    p = m.plan(1, 32, 32, 128, 1, 4096, 0, 0, 0, 256)
+    assert p.grid_x * p.grid_y * p.grid_z >= 256       # at least one workgroup per CU
+    p = m.plan(4, 64, 8, 128, 8, 32768, 1, 1, 0, 256)
+    assert p.grid_x * p.grid_y * p.grid_z >= 256
+
+
+def test_plan_rejects_bad_arguments():
+    with pytest.raises(m.MxfaError):
+        m.plan(1, 8, 2, 100, 1, 64)
+    with pytest.raises(m.MxfaError):
+        m.plan(1, 8, 2, 128, 1, 64, num_splits=-1)
+    assert m.lib().mxfa_plan(1, 8, 2, 128, 1, 64, 0, 0, 0, 0, None) == INV

@@ -1,0 +1,237 @@
+"""GPU path vs the fp64 oracle (needs an MI355X).
+
+Small and medium shapes are compared element by element over every output;
+the full-size long-KV workloads are run in the launch configuration the
+benchmark times (auto partitioning, caller workspace) and checked on sampled
+rows that the oracle computes one by one, plus properties that hold at any
+size.  Every cache slot past a sequence's valid length is NaN (see
+workloads.py), so any read of it would show up as a non-finite output.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import pins
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the -m gpu tests need an MI355X")
+    import split_kv_decode_amd as mx
+    mx.lib()
+    oracle.build()
+
+
+def _full_check(inp, num_splits=0, use_workspace=True, lse_rel=0.0):
+    out, lse, plan = parity.run_gpu(inp, num_splits, use_workspace)
+    ref_o, ref_l = parity.oracle_full(inp)
+    rep = parity.compare(out, lse, ref_o, ref_l, inp.workload.dtype, lse_rel)
+    print(inp.workload.name, plan, rep, flush=True)
+    return out, lse, plan
+
+
+# ------------------------------------------------------------ named workloads
+
+def test_tiny_causal_full():
+    inp = wl.make_inputs(wl.WORKLOADS["tiny_causal"])
+    _full_check(inp)
+    _full_check(inp, use_workspace=False)
+
+
+@pytest.mark.parametrize("name", wl.SMALLQ_NAMES)
+def test_smallq_mha_full(name):
+    _full_check(wl.make_inputs(wl.WORKLOADS[name]))
+
+
+@pytest.mark.parametrize("name", wl.LONG_KV_NAMES)
+def test_long_kv_reduced_full(name):
+    """Same structure at a size the oracle checks completely: several
+    partitions, a ragged tail and (for the ragged workloads) varied lengths."""
+    w = wl.WORKLOADS[name]
+    cap = 2500 if w.len_range else 3000
+    small = wl.scaled(w, B=min(w.B, 5), kv_cap=cap,
+                      len_range=(cap // 4, cap) if w.len_range else None)
+    _full_check(wl.make_inputs(small))
+
+
+@pytest.mark.parametrize("name", wl.LONG_KV_NAMES)
+def test_long_kv_full_size_sampled(name):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    out, lse, plan = parity.run_gpu(inp)
+    assert np.isfinite(out).all()
+    lens = inp.lengths()
+    rows = parity.sample_rows(w, lens, 96 if w.qLen == 1 else 48)
+    rep = parity.check_rows(inp, out, lse, rows)
+    print(name, plan, rep, flush=True)
+    # at every row: O is a convex combination of V rows, so |O| <= max |V|
+    vmax = max(float(inp.v_cache[b, :n].abs().max()) for b, n in enumerate(lens) if n > 0)
+    assert np.abs(out).max() <= vmax * (1 + 2 ** -7)
+    assert np.isfinite(lse).all()
+
+
+# ------------------------------------------------------------ partitioning
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 64, 10 ** 6])
+def test_forced_splits(num_splits):
+    w = wl.Workload("splits", B=3, qLen=2, Hq=8, Hkv=2, D=128, kv_cap=777, dtype="bf16",
+                    causal=True, sigma=1.0, seed=17, len_range=(1, 777))
+    inp = wl.make_inputs(w, lengths=[777, 300, 1])
+    out, lse, plan = _full_check(inp, num_splits=num_splits)
+    assert 1 <= plan["num_splits"] <= min(num_splits, 777)
+
+
+def test_splits_agree_with_each_other():
+    """Different partition counts change only the fp32 summation order."""
+    w = wl.Workload("agree", B=2, qLen=1, Hq=8, Hkv=2, D=128, kv_cap=4096, dtype="fp16",
+                    causal=False, sigma=1.0, seed=23)
+    inp = wl.make_inputs(w)
+    outs = [parity.run_gpu(inp, s)[:2] for s in (1, 4, 16, 64)]
+    for o, l in outs[1:]:
+        assert np.abs(o - outs[0][0]).max() <= 2 * 2 ** -10 * np.abs(outs[0][0]).max()
+        assert np.abs(l - outs[0][1]).max() <= 1e-5
+
+
+def test_deterministic_run_to_run():
+    inp = wl.make_inputs(wl.scaled(wl.WORKLOADS["qwen3_8b_decode"], B=8, kv_cap=4096,
+                                   len_range=(1000, 4096)))
+    o1, l1, _ = parity.run_gpu(inp)
+    o2, l2, _ = parity.run_gpu(inp)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------------------ shapes and edges
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("G,qLen,causal", [(1, 1, False), (2, 1, False), (4, 1, False),
+                                          (8, 1, False), (1, 3, True), (3, 1, False),
+                                          (5, 2, True), (4, 4, True), (8, 8, True),
+                                          (16, 2, False)])
+def test_shape_sweep(D, dtype, G, qLen, causal):
+    Hkv = 2
+    w = wl.Workload("sweep", B=2, qLen=qLen, Hq=G * Hkv, Hkv=Hkv, D=D, kv_cap=1100,
+                    dtype=dtype, causal=causal, sigma=1.0, seed=1000 + G * 10 + qLen,
+                    len_range=(1, 1100))
+    inp = wl.make_inputs(w, lengths=[1100, 613])
+    _full_check(inp)
+
+
+@pytest.mark.parametrize("kvlen", [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 1025])
+def test_kv_length_sweep(kvlen):
+    w = wl.Workload("lens", B=1, qLen=1, Hq=4, Hkv=1, D=128, kv_cap=kvlen, dtype="fp16",
+                    causal=False, sigma=1.0, seed=kvlen)
+    _full_check(wl.make_inputs(w))
+
+
+def test_single_key_output_is_the_v_row_exactly():
+    for dt in ("fp16", "bf16"):
+        w = wl.Workload("one", B=3, qLen=1, Hq=8, Hkv=2, D=128, kv_cap=1, dtype=dt,
+                        causal=False, sigma=1.0, seed=5)
+        inp = wl.make_inputs(w)
+        out, lse, _ = parity.run_gpu(inp)
+        v = inp.v_cache.double().numpy()
+        for h in range(8):
+            assert np.array_equal(out[:, 0, h], v[:, 0, h // 4])
+
+
+def test_empty_rows_and_zero_lengths():
+    w = wl.Workload("empty", B=4, qLen=4, Hq=4, Hkv=2, D=64, kv_cap=50, dtype="bf16",
+                    causal=True, sigma=1.0, seed=9, len_range=(0, 50))
+    inp = wl.make_inputs(w, lengths=[0, 2, 50, 3])
+    out, lse, _ = _full_check(inp)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.all(np.isneginf(lse[1][:, :2]))           # rows 0,1 see nothing with n=2
+    for ns in (1, 5):
+        _full_check(inp, num_splits=ns)
+
+
+def test_zero_capacity_cache():
+    w = wl.Workload("cap0", B=2, qLen=1, Hq=2, Hkv=1, D=128, kv_cap=0, dtype="fp16",
+                    causal=False, sigma=1.0, seed=1)
+    inp = wl.make_inputs(w)
+    out, lse, _ = parity.run_gpu(inp)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_out_of_range_seqlens_are_clamped():
+    w = wl.Workload("clamp", B=3, qLen=1, Hq=4, Hkv=2, D=128, kv_cap=40, dtype="fp16",
+                    causal=False, sigma=1.0, seed=3, len_range=(0, 40))
+    inp = wl.make_inputs(w, lengths=[40, 40, 0])
+    inp.cache_seqlens = torch.tensor([1000, 40, -7], dtype=torch.int32)
+    out, lse, _ = parity.run_gpu(inp)
+    ref_o, ref_l = parity.oracle_full(inp)
+    parity.compare(out, lse, ref_o, ref_l, "fp16")
+
+
+def test_fp16_large_scores_do_not_overflow():
+    """Scores far beyond the fp16 range (|s| ~ 1e4) must stay finite."""
+    g = torch.Generator().manual_seed(31)
+    w = wl.Workload("ovf", B=1, qLen=2, Hq=4, Hkv=1, D=128, kv_cap=300, dtype="fp16",
+                    causal=True, sigma=1.0, seed=31)
+    inp = wl.make_inputs(w)
+    inp.q = (torch.randn(1, 2, 4, 128, generator=g) * 200).to(torch.float16)
+    inp.k_cache = (torch.randn(1, 300, 1, 128, generator=g) * 200).to(torch.float16)
+    out, lse, _ = parity.run_gpu(inp)
+    ref_o, ref_l = parity.oracle_full(inp)
+    assert np.abs(ref_l).max() > 1e4
+    parity.compare(out, lse, ref_o, ref_l, "fp16", lse_rel=2 ** -22)
+
+
+def test_identical_keys_give_the_mean_of_v():
+    w = wl.Workload("ident", B=1, qLen=1, Hq=4, Hkv=1, D=128, kv_cap=3000, dtype="bf16",
+                    causal=False, sigma=1.0, seed=41)
+    inp = wl.make_inputs(w)
+    inp.k_cache = inp.k_cache[:, :1].expand(1, 3000, 1, 128).contiguous()
+    out, lse, _ = parity.run_gpu(inp)
+    mean = inp.v_cache.double().numpy()[0, :, 0].mean(axis=0)
+    assert np.abs(out[0, 0] - mean).max() <= 2 * parity.ulp(np.abs(mean).max(), "bf16")
+    s = inp.q.double().numpy()[0, 0] @ inp.k_cache.double().numpy()[0, 0, 0] / math.sqrt(128)
+    assert np.abs(lse[0, :, 0] - (s + math.log(3000))).max() <= 1e-3
+
+
+def test_golden_examples_on_gpu():
+    """The hand-worked D=4 examples, embedded in D=64: the extra channels are
+    zero and q is multiplied by 4 (exact), so that q.k/sqrt(64) equals the
+    original q.k/sqrt(4) and the expected outputs and lse are unchanged."""
+    import split_kv_decode_amd as mx
+    for ex in pins.load_golden():
+        q, k, v, sl = pins.golden_inputs(ex)
+        eo, el = pins.golden_expected(ex)
+        pad = lambda t: torch.nn.functional.pad(t, (0, 64 - t.shape[-1]))
+        q64, k64, v64 = pad(q * 4), pad(k), pad(v)
+        assert torch.equal((q64[..., :4] / 4), q)
+        dev = lambda t: t.contiguous().to("cuda")
+        sld = None if sl is None else torch.from_numpy(sl).to("cuda")
+        for ns in (0, 2):
+            out, lse = mx.fwd_kvcache(dev(q64), dev(k64), dev(v64), sld, ex["causal"],
+                                      num_splits=ns)
+            torch.cuda.synchronize()
+            o = parity.to_f64(out)
+            assert np.all(o[..., 4:] == 0)
+            parity.compare(o[..., :4], lse.cpu().double().numpy(), eo, el, ex["dtype"])
+
+
+def test_workspace_errors_on_gpu():
+    import split_kv_decode_amd as mx
+    w = wl.Workload("ws", B=2, qLen=1, Hq=8, Hkv=2, D=128, kv_cap=4096, dtype="fp16",
+                    causal=False, sigma=1.0, seed=2)
+    g = wl.make_inputs(w).to("cuda")
+    need = mx.workspace_size(2, 8, 2, 128, 1, 4096, False, 0, 8)
+    assert need > 0
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    out = torch.full_like(g.q, 7.0)
+    with pytest.raises(mx.MxfaError) as e:
+        mx.fwd_kvcache(g.q, g.k_cache, g.v_cache, None, False, out=out, num_splits=8,
+                       workspace=small)
+    assert e.value.status == 3
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())          # untouched on error
