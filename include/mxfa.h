@@ -43,8 +43,9 @@
  *
  * Ownership and threading: the caller owns every buffer.  The library keeps
  * no pointer after a call returns.  Its only mutable state is the
- * thread-local record of the last plan and a per-device cache of the CU
- * count, so calls from several host threads are safe.
+ * thread-local record of the last plan, the thread-local timing hook (see
+ * mxfa_set_timing_events) and a per-device cache of the CU count, so calls
+ * from several host threads are safe.
  *
  * Asynchrony: kernels are enqueued on `stream` (a hipStream_t; NULL = the
  * null stream) and the call returns without synchronising.  The status
@@ -91,14 +92,23 @@ typedef enum {
  * "Python API" section): which kernel path ran and with what partitioning. */
 typedef struct {
     int path;            /* mxfa_path */
+    int layout;          /* VALU path: 0 = each wave slot a different kv head,
+                            2 head groups per workgroup; 1 = same with one
+                            head group; 2 = one kv head per workgroup */
+    int schedule;        /* 0 = fixed partitions of `chunk` tokens per stream;
+                            1 = balanced: grid_x workgroups share the
+                            concatenated KV streams of all sequences equally */
     int rows;            /* R = (Hq / Hkv) * qLen query rows per kv head */
     int row_block;       /* query rows handled by one workgroup */
-    int num_splits;      /* S: KV partitions per (batch, kv head) at kv_cap */
-    int chunk;           /* tokens per partition (the last one may be shorter) */
-    int grid_x, grid_y, grid_z;  /* split-kernel grid (partitions, head/row blocks, batch) */
-    int combine;         /* 1 if the merge kernel runs (S > 1), else 0 */
+    int head_block;      /* kv heads handled by one workgroup */
+    int num_splits;      /* fixed: KV partitions per stream at kv_cap;
+                            balanced: number of workgroups */
+    int chunk;           /* fixed: tokens per partition (the last one may be
+                            shorter); balanced: 0 (set on the device) */
+    int grid_x, grid_y, grid_z;  /* split-kernel grid: partitions, head blocks x row blocks, batch */
+    int combine;         /* 1 if the merge kernel runs, else 0 */
     int num_cus;         /* compute units the plan was made for */
-    size_t workspace_bytes;      /* device scratch the call needs (0 if S == 1) */
+    size_t workspace_bytes;      /* device scratch the call needs (0 without merge) */
 } mxfa_plan_t;
 
 /* Split-KV decode attention, library-managed scratch.

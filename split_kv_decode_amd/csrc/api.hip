@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/mxfa.h: argument checks (pure
 // host code, run before any HIP call), the partitioning planner, scratch
 // management and kernel launches.
-#include "../../include/mxfa.h"
+#include "mxfa.h"
 #include "launch.h"
 
 #include <atomic>
@@ -51,6 +51,8 @@ mxfa_status check_problem(const Problem &p) {
         return MXFA_ERR_INVALID_ARG;
     if (p.D != 64 && p.D != 128) return MXFA_ERR_UNSUPPORTED;
     if (p.B > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
+    // K/V are addressed with 32-bit byte offsets inside one sequence
+    if ((uint64_t)p.kv_cap * p.Hkv * p.D * 2 > (UINT64_C(1) << 30)) return MXFA_ERR_UNSUPPORTED;
     return MXFA_OK;
 }
 
@@ -73,18 +75,51 @@ int next_pow2_le8(int r) { return r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8; }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Partitioning.  Each (batch, kv head, row block) is one unit of work; the
-// KV axis of a unit is cut into S partitions of `chunk` tokens so that the
-// grid holds about 16 workgroups per CU at full length (several waves of
-// workgroups absorb the length spread of a ragged batch), while a partition
-// keeps at least kMinChunk tokens so the partial results stay a small
-// fraction of the K/V traffic.  The SmallQ README derives its KV block from
-// the on-chip buffer size; here the on-chip tile is fixed per kernel and the
-// planner only chooses the partition length.
-mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, mxfa_plan_t *plan) {
-    constexpr int kMinChunk = 256;
+// Slot layout of the VALU kernel: whole head groups when Hkv allows it, so
+// that a workgroup streams whole token rows of the cache (all heads side by
+// side), else one head per workgroup.
+int valu_layout(int Hkv, int D, int *heads_per_block) {
+    const int tpw = 64 / (D / 8);
+    if (Hkv % (2 * tpw) == 0) {
+        *heads_per_block = 2 * tpw;
+        return kHeadsX2;
+    }
+    if (Hkv % tpw == 0) {
+        *heads_per_block = tpw;
+        return kHeadsX1;
+    }
+    *heads_per_block = 1;
+    return kTokens;
+}
+
+// Partitioning (see launch.h for the two schedules).
+//   Fixed partitions: a workgroup serves one (sequence, head block, row block)
+//   stream and one partition of `chunk` tokens of it.  The partition length
+//   is chosen so that the grid holds about kTargetPerCU workgroups per CU at
+//   full length, but no shorter than a floor that keeps the partial results
+//   (row_block x (D + 1) floats per head, written once, read once by the
+//   merge) a small fraction of the partition's K/V bytes.
+//   Balanced: a fixed grid of kBalancedPerCU workgroups per CU, each taking
+//   an equal share (at least the same floor) of all streams laid end to end,
+//   so ragged batches keep every workgroup equally busy.
+// The balanced schedule is used when the planner is free to choose
+// (num_splits = 0), the problem needs more than one partition and the batch
+// fits the kernel's on-chip length table; a forced num_splits selects fixed
+// partitions.  The SmallQ README derives its KV block from the on-chip buffer
+// size; here the on-chip tile is fixed per kernel and only the work split is
+// planned.
+struct FullPlan {
+    mxfa_plan_t pub;
+    int head_blocks, row_blocks, min_share;
+    size_t o_bytes, lse_bytes, cum_bytes;
+};
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *fp) {
     constexpr int kChunkAlign = 64;
-    constexpr int kTargetPerCU = 16;
+    constexpr int kTargetPerCU = 8;
+    constexpr int kBalancedPerCU = 2;
     mxfa_plan_t pl;
     std::memset(&pl, 0, sizeof(pl));
     if (num_cus <= 0) num_cus = kDefaultCUs;
@@ -95,8 +130,15 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, mxfa_plan_t
     pl.rows = (int)R;
     pl.row_block = next_pow2_le8((int)R);
     const int row_blocks = R > 0 ? ceil_div(R, pl.row_block) : 1;
-    if ((long long)p.Hkv * row_blocks > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
+    int hpb = 1;
+    pl.layout = valu_layout(p.Hkv, p.D, &hpb);
+    pl.head_block = hpb;
+    const int head_blocks = ceil_div(p.Hkv, hpb);
+    if ((long long)head_blocks * row_blocks > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
     pl.num_cus = num_cus;
+    const long long streams = (long long)p.B * head_blocks * row_blocks;
+    const int min_chunk =
+        ceil_div(16 * pl.row_block > 64 ? 16 * pl.row_block : 64, kChunkAlign) * kChunkAlign;
 
     int S, chunk;
     if (p.kv_cap == 0) {
@@ -107,29 +149,50 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, mxfa_plan_t
         chunk = ceil_div(p.kv_cap, S);
         S = ceil_div(p.kv_cap, chunk);
     } else {
-        const long long base = (long long)p.B * p.Hkv * row_blocks;
         const long long target = (long long)num_cus * kTargetPerCU;
-        long long want = base > 0 ? (target + base - 1) / base : 1;
-        const long long smax = (p.kv_cap + kMinChunk - 1) / kMinChunk;
+        long long want = streams > 0 ? (target + streams - 1) / streams : 1;
+        const long long smax = (p.kv_cap + min_chunk - 1) / min_chunk;
         if (want > smax) want = smax;
         if (want < 1) want = 1;
         chunk = ceil_div(p.kv_cap, want);
         chunk = ceil_div(chunk, kChunkAlign) * kChunkAlign;
         S = ceil_div(p.kv_cap, chunk);
     }
-    pl.num_splits = S;
-    pl.chunk = chunk;
-    pl.grid_x = S;
-    pl.grid_y = p.Hkv * row_blocks;
-    pl.grid_z = p.B;
-    pl.combine = S > 1 ? 1 : 0;
-    if (pl.combine) {
-        const size_t rows = (size_t)p.B * p.Hq * p.qLen * S;
-        const size_t o_bytes = (rows * p.D * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
-        const size_t l_bytes = (rows * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
-        pl.workspace_bytes = o_bytes + l_bytes;
+    long long slots;
+    if (num_splits == 0 && S > 1 && p.B <= kMaxBalancedBatch) {
+        pl.schedule = kBalanced;
+        const int P = num_cus * kBalancedPerCU;
+        pl.num_splits = P;
+        pl.chunk = 0;
+        pl.grid_x = P;
+        pl.grid_y = 1;
+        pl.grid_z = 1;
+        pl.combine = 1;
+        slots = P + streams;
+    } else {
+        pl.schedule = kFixed;
+        pl.num_splits = S;
+        pl.chunk = chunk;
+        pl.grid_x = S;
+        pl.grid_y = head_blocks * row_blocks;
+        pl.grid_z = p.B;
+        pl.combine = S > 1 ? 1 : 0;
+        slots = streams * S;
     }
-    *plan = pl;
+    FullPlan f;
+    std::memset(&f, 0, sizeof(f));
+    if (pl.combine) {
+        const size_t entries = (size_t)slots * hpb * pl.row_block;
+        f.o_bytes = align_up(entries * p.D * sizeof(float));
+        f.lse_bytes = align_up(entries * sizeof(float));
+        f.cum_bytes = pl.schedule == kBalanced ? align_up((size_t)(p.B + 2) * sizeof(long long)) : 0;
+        pl.workspace_bytes = f.o_bytes + f.lse_bytes + f.cum_bytes;
+    }
+    f.pub = pl;
+    f.head_blocks = head_blocks;
+    f.row_blocks = row_blocks;
+    f.min_share = min_chunk;
+    *fp = f;
     return MXFA_OK;
 }
 
@@ -153,53 +216,45 @@ mxfa_status device_cus(int *cus) {
 }
 
 mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seqlens,
-                void *out, float *lse, const Problem &p, const mxfa_plan_t &pl,
-                void *ws, hipStream_t stream) {
-    SplitArgs sa;
-    sa.q = q;
-    sa.k = k;
-    sa.v = v;
-    sa.seqlens = seqlens;
-    sa.out = out;
-    sa.lse = lse;
-    sa.ws_o = nullptr;
-    sa.ws_lse = nullptr;
+                void *out, float *lse, const Problem &p, const FullPlan &f, void *ws,
+                hipStream_t stream) {
+    const mxfa_plan_t &pl = f.pub;
+    KernelArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.seqlens = seqlens;
+    a.out = out;
+    a.lse = lse;
     if (pl.combine) {
-        const size_t rows = (size_t)p.B * p.Hq * p.qLen * pl.num_splits;
-        const size_t o_bytes = (rows * p.D * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
-        sa.ws_o = (float *)ws;
-        sa.ws_lse = (float *)((char *)ws + o_bytes);
+        a.ws_o = (float *)ws;
+        a.ws_lse = (float *)((char *)ws + f.o_bytes);
+        a.ws_cum = f.cum_bytes ? (int *)((char *)ws + f.o_bytes + f.lse_bytes) : nullptr;
     }
-    sa.B = p.B;
-    sa.Hq = p.Hq;
-    sa.Hkv = p.Hkv;
-    sa.qLen = p.qLen;
-    sa.kv_cap = p.kv_cap;
-    sa.G = p.Hq / p.Hkv;
-    sa.R = pl.rows;
-    sa.chunk = pl.chunk;
-    sa.S = pl.num_splits;
-    sa.qscale = (float)(1.4426950408889634 / std::sqrt((double)p.D));
+    a.B = p.B;
+    a.Hq = p.Hq;
+    a.Hkv = p.Hkv;
+    a.qLen = p.qLen;
+    a.kv_cap = p.kv_cap;
+    a.G = p.Hq / p.Hkv;
+    a.R = pl.rows;
+    a.D = p.D;
+    a.causal = p.causal;
+    a.head_block = pl.head_block;
+    a.head_blocks = f.head_blocks;
+    a.row_block = pl.row_block;
+    a.row_blocks = f.row_blocks;
+    a.schedule = pl.schedule;
+    a.chunk = pl.chunk;
+    a.S = pl.num_splits;
+    a.min_share = f.min_share;
+    a.qscale = (float)(1.4426950408889634 / std::sqrt((double)p.D));
     const dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z);
     if (t_ev_before && hipEventRecord(t_ev_before, stream) != hipSuccess) return MXFA_ERR_HIP;
-    if (launch_split_valu(sa, p.dtype, p.D, pl.row_block, p.causal, grid, stream) != hipSuccess)
-        return MXFA_ERR_HIP;
+    if (launch_split_valu(a, p.dtype, pl.layout, grid, stream) != hipSuccess) return MXFA_ERR_HIP;
     if (t_ev_after && hipEventRecord(t_ev_after, stream) != hipSuccess) return MXFA_ERR_HIP;
-    if (pl.combine) {
-        CombineArgs ca;
-        ca.ws_o = sa.ws_o;
-        ca.ws_lse = sa.ws_lse;
-        ca.seqlens = seqlens;
-        ca.out = out;
-        ca.lse = lse;
-        ca.B = p.B;
-        ca.Hq = p.Hq;
-        ca.qLen = p.qLen;
-        ca.kv_cap = p.kv_cap;
-        ca.chunk = pl.chunk;
-        ca.S = pl.num_splits;
-        if (launch_combine(ca, p.dtype, p.D, stream) != hipSuccess) return MXFA_ERR_HIP;
-    }
+    if (pl.combine && launch_combine(a, p.dtype, stream) != hipSuccess) return MXFA_ERR_HIP;
     return MXFA_OK;
 }
 
@@ -219,7 +274,10 @@ MXFA_API mxfa_status mxfa_plan(int B, int Hq, int Hkv, int D, int qLen, int kv_c
     const Problem p{B, Hq, Hkv, D, qLen, kv_cap, causal, dtype};
     mxfa_status st = check_problem(p);
     if (st != MXFA_OK) return st;
-    return make_plan(p, num_splits, num_cus, plan);
+    FullPlan f;
+    st = make_plan(p, num_splits, num_cus, &f);
+    if (st == MXFA_OK) *plan = f.pub;
+    return st;
 }
 
 MXFA_API mxfa_status mxfa_workspace_size(int B, int Hq, int Hkv, int D, int qLen, int kv_cap,
@@ -232,10 +290,10 @@ MXFA_API mxfa_status mxfa_workspace_size(int B, int Hq, int Hkv, int D, int qLen
     int cus = 0;
     st = device_cus(&cus);
     if (st != MXFA_OK) return st;
-    mxfa_plan_t pl;
-    st = make_plan(p, num_splits, cus, &pl);
+    FullPlan f;
+    st = make_plan(p, num_splits, cus, &f);
     if (st != MXFA_OK) return st;
-    *bytes = (B == 0 || qLen == 0) ? 0 : pl.workspace_bytes;
+    *bytes = (B == 0 || qLen == 0) ? 0 : f.pub.workspace_bytes;
     return MXFA_OK;
 }
 
@@ -255,13 +313,13 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_ws(const void *q, const void *k_cache, con
     int cus = 0;
     st = device_cus(&cus);
     if (st != MXFA_OK) return st;
-    mxfa_plan_t pl;
-    st = make_plan(p, num_splits, cus, &pl);
+    FullPlan f;
+    st = make_plan(p, num_splits, cus, &f);
     if (st != MXFA_OK) return st;
-    if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
+    if (f.pub.workspace_bytes > 0 && (!workspace || workspace_bytes < f.pub.workspace_bytes))
         return MXFA_ERR_WORKSPACE;
-    st = run(q, k_cache, v_cache, cache_seqlens, out, lse, p, pl, workspace, (hipStream_t)stream);
-    if (st == MXFA_OK) record(pl);
+    st = run(q, k_cache, v_cache, cache_seqlens, out, lse, p, f, workspace, (hipStream_t)stream);
+    if (st == MXFA_OK) record(f.pub);
     return st;
 }
 
@@ -278,16 +336,16 @@ MXFA_API mxfa_status mxfa_fwd_kvcache(const void *q, const void *k_cache, const 
     int cus = 0;
     st = device_cus(&cus);
     if (st != MXFA_OK) return st;
-    mxfa_plan_t pl;
-    st = make_plan(p, 0, cus, &pl);
+    FullPlan f;
+    st = make_plan(p, 0, cus, &f);
     if (st != MXFA_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     void *ws = nullptr;
-    if (pl.workspace_bytes > 0 && hipMallocAsync(&ws, pl.workspace_bytes, s) != hipSuccess)
+    if (f.pub.workspace_bytes > 0 && hipMallocAsync(&ws, f.pub.workspace_bytes, s) != hipSuccess)
         return MXFA_ERR_HIP;
-    st = run(q, k_cache, v_cache, cache_seqlens, out, lse, p, pl, ws, s);
+    st = run(q, k_cache, v_cache, cache_seqlens, out, lse, p, f, ws, s);
     if (ws && hipFreeAsync(ws, s) != hipSuccess && st == MXFA_OK) st = MXFA_ERR_HIP;
-    if (st == MXFA_OK) record(pl);
+    if (st == MXFA_OK) record(f.pub);
     return st;
 }
 

@@ -9,82 +9,150 @@
 //     O = sum_s w_s O_s / L,  lse = (M + log2 L) * ln 2   (natural log).
 // A row whose partitions all saw no key (M = -inf) gets O = 0, lse = -inf.
 //
-// One wave per output row (b, h, i); lanes split the D channels.  Only the
-// n_s = ceil(n_b / chunk) partitions that exist for sequence b are read.
+// One wave per output row (b, h, i).  The row belongs to the stream of its
+// (sequence, head block, row block); the slots that hold the stream's
+// partials are consecutive (see launch.h): with fixed partitions the
+// ceil(n_b / chunk) partitions of the stream, with the balanced schedule the
+// workgroups whose share of the concatenated streams overlaps it.  A stream
+// served by one workgroup was written directly by the split kernel and is
+// skipped; a stream with no token at all gets O = 0, lse = -inf here.  The
+// weights are computed
+// with one partition per lane and kept in LDS; the weighted sum then splits
+// the wave into NG groups of D/4 lanes (4 channels per lane, 16-byte loads),
+// each group taking every NG-th partition with UNR loads in flight, and the
+// groups are summed with cross-lane exchanges.
 #include "device_common.h"
 #include "launch.h"
 
 namespace mxfa {
 namespace {
 
+constexpr int kRowsPerBlock = 4;
+constexpr int kMaxStaged = 256;     // weights staged in LDS per pass
+
 template <int DT, int D>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-    constexpr int PER = D / 64;                 // channels per lane (1 or 2)
+__global__ __launch_bounds__(kRowsPerBlock * 64) void combine_kernel(KernelArgs a) {
+    constexpr int LPG = D / 4;                  // lanes per group
+    constexpr int NG = 64 / LPG;                // groups per wave (2 or 4)
+    constexpr int UNR = 4;
+    __shared__ float lds_w[kRowsPerBlock][kMaxStaged];
+
     const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
+    const long long row = (long long)blockIdx.x * kRowsPerBlock + wave;
     const long long nrows = (long long)a.B * a.Hq * a.qLen;
-    if (row >= nrows) return;
+    if (row >= nrows) return;                   // whole wave exits together
     const int i = (int)(row % a.qLen);
     const int h = (int)((row / a.qLen) % a.Hq);
     const int b = (int)(row / ((long long)a.qLen * a.Hq));
+    const int kvh = h / a.G;
+    const int rg = i * a.G + h % a.G;           // row index within the kv head
+    const int hb = kvh / a.head_block, hx = kvh % a.head_block;
+    const int rb = rg / a.row_block, r = rg % a.row_block;
+    const int HR = a.head_blocks * a.row_blocks;
+    const int jst = hb * a.row_blocks + rb;     // stream index within sequence b
+    const int st = b * HR + jst;
 
     const int n = clampi(a.seqlens ? a.seqlens[b] : a.kv_cap, 0, a.kv_cap);
-    const int ns = clampi((n + a.chunk - 1) / a.chunk, 1, a.S);
-    const float *lrow = a.ws_lse + (size_t)row * a.S;   // row = (b*Hq + h)*qLen + i
-    const float *orow = a.ws_o + (size_t)row * a.S * D;
+    long long first;
+    int count;
+    if (a.schedule == kFixed) {
+        count = (n + a.chunk - 1) / a.chunk;
+        first = (long long)st * a.S;
+    } else if (n > 0) {
+        const long long *cw = (const long long *)a.ws_cum;
+        const long long W = cw[a.B + 1];
+        const long long c0 = cw[b] * HR + (long long)jst * n;   // stream start
+        const long long w_lo = c0 / W, w_hi = (c0 + n - 1) / W;
+        count = (int)(w_hi - w_lo + 1);
+        first = w_lo + st;
+    } else {
+        count = 0;
+        first = 0;
+    }
+    if (count == 1) return;                     // written by the split kernel
+
+    const size_t stride = (size_t)a.head_block * a.row_block;   // entries per slot
+    const size_t e0 = ((size_t)first * a.head_block + hx) * a.row_block + r;
+    const float *lrow = a.ws_lse + e0;           // entry of slot k at lrow[k * stride]
+    const float *orow = a.ws_o + e0 * D;         // row of slot k at orow[k * stride * D]
 
     float M = kNegInf;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, lrow[s]);
+    for (int s = lane; s < count; s += 64) M = fmaxf(M, lrow[(size_t)s * stride]);
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
 
-    float acc[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+    const int g = lane / LPG;
+    const int d0 = (lane % LPG) * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     if (M != kNegInf) {
-        for (int s = 0; s < ns; ++s) {
-            const float w = fast_exp2(lrow[s] - M);   // -inf partitions weigh 0
-            L += w;
-            const float *op = orow + (size_t)s * D + lane * PER;
-            if constexpr (PER == 2) {
-                const f32x2 x = *(const f32x2 *)op;
-                acc[0] = fmaf(w, x[0], acc[0]);
-                acc[1] = fmaf(w, x[1], acc[1]);
-            } else {
-                acc[0] = fmaf(w, op[0], acc[0]);
+        for (int s0 = 0; s0 < count; s0 += kMaxStaged) {
+            const int cnt = min(count - s0, kMaxStaged);
+            for (int s = lane; s < cnt; s += 64) {
+                const float w = fast_exp2(lrow[(size_t)(s0 + s) * stride] - M);
+                lds_w[wave][s] = w;                     // -inf partials weigh 0
+                L += w;
             }
+            wave_lds_sync();
+            int s = g;
+            for (; s + (UNR - 1) * NG < cnt; s += UNR * NG) {
+                f32x4 x[UNR];
+#pragma unroll
+                for (int u = 0; u < UNR; ++u)
+                    x[u] = *(const f32x4 *)(orow + (size_t)(s0 + s + u * NG) * stride * D + d0);
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    const float w = lds_w[wave][s + u * NG];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, x[u][j], acc[j]);
+                }
+            }
+            for (; s < cnt; s += NG) {
+                const f32x4 x = *(const f32x4 *)(orow + (size_t)(s0 + s) * stride * D + d0);
+                const float w = lds_w[wave][s];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, x[j], acc[j]);
+            }
+            wave_lds_sync();
         }
     }
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
+#pragma unroll
+    for (int x = LPG; x < 64; x <<= 1)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], x);
+
     const bool empty = !(L > 0.f);
     const float inv = empty ? 0.f : 1.f / L;
-    uint16_t *outp = (uint16_t *)a.out + (((size_t)b * a.qLen + i) * a.Hq + h) * D + lane * PER;
-    if constexpr (PER == 2)
-        *(uint32_t *)outp = pack2<DT>(acc[0] * inv, acc[1] * inv);
-    else
-        *outp = (uint16_t)to16<DT>(acc[0] * inv);
+    if (g == 0) {
+        uint16_t *outp = (uint16_t *)a.out + (((size_t)b * a.qLen + i) * a.Hq + h) * D + d0;
+        *(u32x2 *)outp = u32x2{pack2<DT>(acc[0] * inv, acc[1] * inv),
+                               pack2<DT>(acc[2] * inv, acc[3] * inv)};
+    }
     if (lane == 0 && a.lse) a.lse[row] = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
 }
 
 template <int DT, int D>
-hipError_t launch_t(const CombineArgs &a, hipStream_t stream) {
-    CombineArgs args = a;
+hipError_t launch_t(const KernelArgs &a, hipStream_t stream) {
+    KernelArgs args = a;
     void *kargs[] = {&args};
     const long long nrows = (long long)a.B * a.Hq * a.qLen;
-    const unsigned blocks = (unsigned)((nrows + 3) / 4);
-    return hipLaunchKernel((const void *)&combine_kernel<DT, D>, dim3(blocks), dim3(256),
-                           kargs, 0, stream);
+    const unsigned blocks = (unsigned)((nrows + kRowsPerBlock - 1) / kRowsPerBlock);
+    return hipLaunchKernel((const void *)&combine_kernel<DT, D>, dim3(blocks),
+                           dim3(kRowsPerBlock * 64), kargs, 0, stream);
 }
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs &a, int dtype, int D, hipStream_t stream) {
+hipError_t launch_combine(const KernelArgs &a, int dtype, hipStream_t stream) {
     if (dtype == kFp16) {
-        if (D == 128) return launch_t<kFp16, 128>(a, stream);
-        if (D == 64) return launch_t<kFp16, 64>(a, stream);
+        if (a.D == 128) return launch_t<kFp16, 128>(a, stream);
+        if (a.D == 64) return launch_t<kFp16, 64>(a, stream);
     } else {
-        if (D == 128) return launch_t<kBf16, 128>(a, stream);
-        if (D == 64) return launch_t<kBf16, 64>(a, stream);
+        if (a.D == 128) return launch_t<kBf16, 128>(a, stream);
+        if (a.D == 64) return launch_t<kBf16, 64>(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -89,6 +89,24 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) {
     return x < lo ? lo : (x > hi ? hi : x);
 }
 
+// Raw buffer descriptor over `bytes` bytes from `base` (stride 0, so the
+// hardware range check applies to the per-lane byte offset: loads at or past
+// `bytes` return zero and do not access memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Cache policy of the streaming K/V loads (0 = default, 2 = non-temporal).
+#ifndef MXFA_KV_LOAD_POLICY
+#define MXFA_KV_LOAD_POLICY 0
+#endif
+
+// 16-byte load through a buffer descriptor (buffer_load_dwordx4).
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, MXFA_KV_LOAD_POLICY);
+}
+
 // Orders this wave's LDS accesses around a point where lanes exchange data
 // through LDS without a workgroup barrier.
 __device__ __forceinline__ void wave_lds_sync() {

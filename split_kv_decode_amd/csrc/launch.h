@@ -6,37 +6,61 @@
 
 namespace mxfa {
 
-// Everything a split kernel needs; pointers are device addresses.
-struct SplitArgs {
+// How the VALU split kernel maps the 16-lane slots of a wave to kv heads:
+// every slot a different head, with 2 or 1 head groups per workgroup
+// (2 * TPW or TPW heads per workgroup, TPW = 64 / (D / 8) slots per wave), or
+// one head per workgroup with the slots on different tokens.
+enum ValuLayout { kHeadsX2 = 0, kHeadsX1 = 1, kTokens = 2 };
+
+// How KV tokens are handed to workgroups.
+//   kFixed:    grid (S, head_blocks * row_blocks, B); workgroup (s, y, b) takes
+//              tokens [s * chunk, (s + 1) * chunk) of its stream.
+//   kBalanced: grid (P); the streams are laid end to end and workgroup w takes
+//              an equal share [w * W, (w + 1) * W) of the concatenation, which
+//              may span several streams (W from the device-side lengths).
+enum Schedule { kFixed = 0, kBalanced = 1 };
+
+// A "stream" is the KV token sequence of one (sequence b, head block hb, row
+// block rb); stream index st = (b * head_blocks + hb) * row_blocks + rb.
+//
+// Partial results live in slots.  A slot holds, for the head_block heads x
+// row_block rows of one stream, the normalised output [hpb][rb][D] (fp32) and
+// the log2-sum-exp [hpb][rb].  Slots of stream st:
+//   kFixed:    st * S + s for the partitions s < ceil(n_b / chunk);
+//   kBalanced: w + st for the workgroups w that touch the stream (these never
+//              collide: a later workgroup only reaches later streams).
+// A workgroup that covers a whole stream writes the final output instead.
+struct KernelArgs {
     const void *q;            // [B, qLen, Hq, D]
     const void *k;            // [B, kv_cap, Hkv, D]
     const void *v;            // [B, kv_cap, Hkv, D]
     const int32_t *seqlens;   // [B] or nullptr
-    void *out;                // [B, qLen, Hq, D]   (written when S == 1)
-    float *lse;               // [B, Hq, qLen] or nullptr (written when S == 1)
-    float *ws_o;              // [B, Hq, qLen, S, D] normalised partial outputs
-    float *ws_lse;            // [B, Hq, qLen, S]    partial lse, log2 units
+    void *out;                // [B, qLen, Hq, D]
+    float *lse;               // [B, Hq, qLen] or nullptr
+    float *ws_o;              // [slots][head_block][row_block][D]
+    float *ws_lse;            // [slots][head_block][row_block]
+    int *ws_cum;              // kBalanced: [B + 1] length prefix sums, then W
     int B, Hq, Hkv, qLen, kv_cap;
     int G;                    // Hq / Hkv
     int R;                    // G * qLen rows per kv head
-    int chunk;                // tokens per partition
-    int S;                    // partitions per (b, kv head) at kv_cap
+    int D;
+    int causal;
+    int head_block, head_blocks;
+    int row_block, row_blocks;
+    int schedule;             // Schedule
+    int chunk;                // kFixed: tokens per partition
+    int S;                    // kFixed: partitions per stream; kBalanced: workgroups P
+    int min_share;            // kBalanced: lower bound on tokens per workgroup
     float qscale;             // log2(e) / sqrt(D)
 };
 
-struct CombineArgs {
-    const float *ws_o;
-    const float *ws_lse;
-    const int32_t *seqlens;
-    void *out;
-    float *lse;
-    int B, Hq, qLen, kv_cap, chunk, S;
-};
+// Largest batch the balanced schedule handles (its length prefix sums are
+// kept in LDS by every workgroup).
+constexpr int kMaxBalancedBatch = 1024;
 
-hipError_t launch_split_valu(const SplitArgs &a, int dtype, int D, int row_block,
-                             int causal, dim3 grid, hipStream_t stream);
+hipError_t launch_split_valu(const KernelArgs &a, int dtype, int layout, dim3 grid,
+                             hipStream_t stream);
 
-hipError_t launch_combine(const CombineArgs &a, int dtype, int D,
-                          hipStream_t stream);
+hipError_t launch_combine(const KernelArgs &a, int dtype, hipStream_t stream);
 
 }  // namespace mxfa

@@ -5,18 +5,24 @@
 // streaming K and V from HBM.
 //
 // Work decomposition.  A workgroup (4 waves) owns one KV partition
-// [split * chunk, (split + 1) * chunk) of one (batch b, kv head) pair for a
-// block of RB query rows -- the split-KV decomposition of the MXFlashAttn
-// package page (M1 split-KV decode), with the K-outer loop and resident Q of
-// the SmallQ FlashAttention README (algorithm notes).  Row r of a block is
-// query position i = r / G and head h = kvh * G + r % G.
+// [split * chunk, (split + 1) * chunk) of one sequence b, for a block of HPW
+// consecutive kv heads and a block of RB query rows per head -- the split-KV
+// decomposition of the MXFlashAttn package page (M1 split-KV decode), with the
+// K-outer loop and resident Q of the SmallQ FlashAttention README (algorithm
+// notes).  Row r of a head's block is query position i = r / G and query head
+// h = kvh * G + r % G.
 //
 // Lane layout.  A token's head slice (D 16-bit values) is read by LPT = D/8
-// lanes, 16 contiguous bytes each (one global_load_dwordx4 per lane, fully
-// coalesced); a wave therefore covers TPW = 64 / LPT tokens per load, one per
-// "token slot" of LPT lanes.  Each lane loads U tokens of K and U of V per
-// step and computes partial dot products over its 8 channels for its U
-// tokens x RB rows (N = U * RB partials, v_dot2 with fp32 accumulation).
+// lanes, 16 contiguous bytes each; such a group of lanes is a "slot", and a
+// wave has TPW = 64 / LPT slots.  Slot s of a wave serves kv head (s % HS) of
+// the wave's head group and token sub-index (s / HS).  With HS = TPW every
+// slot is a different head of the same token, so one load instruction reads
+// one contiguous stretch of a token row (the heads sit side by side in the
+// [B, kv_cap, Hkv, D] cache) and the workgroup streams whole token rows.  The
+// workgroup's waves cover HG head groups x TI token interleaves (HG * TI = 4).
+// Each lane loads U tokens of K and of V per step and computes partial dot
+// products over its 8 channels for U tokens x RB rows (N = U * RB partials,
+// v_dot2 with fp32 accumulation).
 //
 // Reduce-scatter.  The N partials are summed across the LPT lanes of the
 // slot with DPP exchanges inside a 16-lane row (xor 8 = row_ror:8, xor 7 =
@@ -31,18 +37,27 @@
 // holds one complete score, for (token u*, row r*) = (phi_u, phi_r).
 //
 // Online softmax (ops-transformer articles: running max m and sum l, with
-// the accumulated output rescaled by exp(m_old - m_new)).  Per token slot and
-// row, in log2 units (Q K^T is scaled by log2(e)/sqrt(D) so exp2 replaces
-// exp): row max over the slot's U tokens by DPP, p = exp2(s - m_new),
+// the accumulated output rescaled by exp(m_old - m_new)).  Per slot and row,
+// in log2 units (Q K^T is scaled by log2(e)/sqrt(D) so exp2 replaces exp):
+// row max over the slot's U tokens by DPP, p = exp2(s - m_new),
 // alpha = exp2(m_old - m_new), l = alpha * l + sum p.  p and alpha are shared
 // within the slot through a small LDS array; the rescale of O is skipped when
 // no row's maximum moved anywhere in the wave.  O += p V in fp32 with V
 // converted from 16 bits (the SmallQ README's fp32 PV accumulation).
 //
-// Epilogue.  The TPW slots of a wave and the 4 waves of the workgroup hold
-// independent (m, l, O) states; they are merged with the same log-sum-exp
-// rule, then written either as the final output (single partition) or as a
-// normalised partial O plus its log2-sum-exp for the combine kernel.
+// Epilogue.  Slots and waves that served the same head hold independent
+// (m, l, O) states for different tokens; they are merged with the same
+// log-sum-exp rule, then written either as the final output (when the
+// workgroup covered the whole KV range of its heads) or as a normalised
+// partial O plus its log2-sum-exp for the combine kernel.
+//
+// Schedules (see launch.h).  With fixed partitions a workgroup processes one
+// segment [split * chunk, ...) of one (sequence, head block, row block)
+// stream.  With the balanced schedule the streams are laid end to end and
+// every workgroup takes an equal share of the concatenation, processing the
+// one or more stream segments that fall into it; this keeps all workgroups
+// equally loaded however ragged the sequence lengths are.  The lengths are
+// read on the device, so each workgroup first forms their prefix sums.
 #include "device_common.h"
 #include "launch.h"
 
@@ -50,6 +65,11 @@ namespace mxfa {
 namespace {
 
 constexpr int kWaves = 4;
+
+// Occupancy target (waves per SIMD) handed to the register allocator.
+#ifndef MXFA_VALU_WAVES_PER_EU
+#define MXFA_VALU_WAVES_PER_EU 2
+#endif
 
 // DPP lane mask used at step t of the reduce sequence for a slot of 2^LB lanes.
 constexpr int step_mask(int LB, int t) {
@@ -91,302 +111,410 @@ struct Halve {
     }
 };
 
-template <int DT, int D, int RB, bool CAUSAL>
-__global__ __launch_bounds__(kWaves * 64) void split_kv_valu_kernel(SplitArgs a) {
-    constexpr int LPT = D / 8;                  // lanes per token
-    constexpr int LB = ilog2(LPT);              // 4 (D=128) or 3 (D=64)
-    constexpr int TPW = 64 / LPT;               // token slots per wave
-    constexpr int U = (LPT / RB) >= 4 ? 4 : (LPT / RB);  // tokens per slot per step
-    constexpr int N = U * RB;                   // partial scores per lane per step
-    constexpr int H = ilog2(N);                 // halving steps
-    constexpr int LOGRB = ilog2(RB);
-    constexpr int LOGU = ilog2(U);
-    constexpr int TPS = TPW * U;                // tokens per wave step
+template <int DT, int D, int RB, int HS, int HG>
+struct Valu {
+    static constexpr int LPT = D / 8;                  // lanes per slot
+    static constexpr int LB = ilog2(LPT);              // 4 (D=128) or 3 (D=64)
+    static constexpr int TPW = 64 / LPT;               // slots per wave
+    static constexpr int TSUB = TPW / HS;              // token sub-slots per wave
+    static constexpr int TI = kWaves / HG;             // token interleave across waves
+    static constexpr int HPW = HG * HS;                // kv heads per workgroup
+    static constexpr int U = (LPT / RB) >= 4 ? 4 : (LPT / RB);  // tokens per slot per step
+    static constexpr int N = U * RB;                   // partial scores per lane per step
+    static constexpr int H = ilog2(N);                 // halving steps
+    static constexpr int LOGRB = ilog2(RB);
+    static constexpr int LOGU = ilog2(U);
+    static constexpr int TSTEP = U * TSUB;             // tokens per wave step
+    static constexpr int NSTATE = TI * TSUB;           // partial states per (head, row)
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(N >= 2 && N <= LPT, "reduce-scatter shape");
+    static_assert(TPW % HS == 0 && kWaves % HG == 0, "slot mapping");
 
-    __shared__ __attribute__((aligned(16))) float lds_p[kWaves][TPW][N];
-    __shared__ __attribute__((aligned(16))) float lds_a[kWaves][TPW][RB];
-    __shared__ __attribute__((aligned(16))) float lds_ml[kWaves][TPW][2][RB];
-    __shared__ __attribute__((aligned(16))) float lds_o[kWaves][RB][D];
-    __shared__ __attribute__((aligned(16))) float lds_wml[kWaves][2][RB];
-
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y % a.Hkv;
-    const int rb = blockIdx.y / a.Hkv;
-    const int b = blockIdx.z;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int sl = lane & (LPT - 1);
-    const int sg = lane >> LB;
-
-    const int n = clampi(a.seqlens ? a.seqlens[b] : a.kv_cap, 0, a.kv_cap);
-    const int t_lo = split * a.chunk;
-    if (split > 0 && t_lo >= n) return;       // partition past this sequence
-    int t_hi = min(t_lo + a.chunk, n);
-    const int row0 = rb * RB;
-    if constexpr (CAUSAL) {
-        // no row of this block sees a key past (last query position) + n - qLen
-        const int i_max = (min(row0 + RB, a.R) - 1) / a.G;
-        t_hi = min(t_hi, i_max + n - a.qLen + 1);
-    }
-    const int nsteps = t_hi > t_lo ? (t_hi - t_lo + TPS - 1) / TPS : 0;
-
-    // lane permutation of the reduce-scatter
-    const int gperm = sl ^ (((sl >> 2) & 1) * 3);
-    const int phi = gperm >> (LB - H);
-    const int phir = phi & (RB - 1);
-    const int phiu = phi >> LOGRB;
-
-    // the score this lane finishes with belongs to row (row0 + phir)
-    const int my_row = row0 + phir;
-    const bool row_ok = my_row < a.R;
-    const int causal_last = my_row / a.G + n - a.qLen;
-
-    // Q rows, resident for the whole partition (16-bit, unscaled)
-    u32x4 qr[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        const int row = row0 + (r ^ phir);
-        if (row < a.R) {
-            const int i = row / a.G;
-            const int h = kvh * a.G + row % a.G;
-            const uint16_t *qp = (const uint16_t *)a.q +
-                                 (((size_t)b * a.qLen + i) * a.Hq + h) * D + 8 * sl;
-            qr[r] = *(const u32x4 *)qp;
-        } else {
-            qr[r] = u32x4{0, 0, 0, 0};
-        }
-    }
-
-    const size_t tok_stride = (size_t)a.Hkv * D;
-    const size_t head_off = ((size_t)b * a.kv_cap * a.Hkv + kvh) * D + 8 * sl;
-    const uint16_t *kbase = (const uint16_t *)a.k + head_off;
-    const uint16_t *vbase = (const uint16_t *)a.v + head_off;
-
-    float m_run = kNegInf, l_run = 0.f;
-    float o[RB][8];
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
-
-    auto load_step = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[U]) {
-        const int base = t_lo + st * TPS + sg;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            // tokens past the partition are masked later; clamping keeps the
-            // address inside the valid part of the cache (never the tail)
-            const int tk = min(base + (u ^ phiu) * TPW, n - 1);
-            const int tv = min(base + u * TPW, n - 1);
-            kr[u] = *(const u32x4 *)(kbase + (size_t)tk * tok_stride);
-            vr[u] = *(const u32x4 *)(vbase + (size_t)tv * tok_stride);
-        }
+    struct Smem {
+        float p[kWaves][TPW][N];
+        float a[kWaves][TPW][RB];
+        float m[NSTATE][HPW][RB];
+        float l[NSTATE][HPW][RB];
+        float o[NSTATE][HPW][RB][D];
     };
 
-    auto compute_step = [&](int st, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
-        float v[N];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                float acc = 0.f;
-                acc = dot2<DT>(qr[r][0], kr[u][0], acc);
-                acc = dot2<DT>(qr[r][1], kr[u][1], acc);
-                acc = dot2<DT>(qr[r][2], kr[u][2], acc);
-                acc = dot2<DT>(qr[r][3], kr[u][3], acc);
-                v[r + RB * u] = acc;
-            }
-        Halve<LB, N, 0, H>::run(v);
-        const float s = AllReduce<LB, H, LB>::sum(v[0]);
+    // Tokens [t_lo, t_hi) of the stream (b, hb, rb); n is sequence b's valid
+    // length.  whole: the segment is the stream's entire range [0, n), so the
+    // final output is written; otherwise the partial goes to `slot`.
+    __device__ static void segment(const KernelArgs &a, Smem &sm, int b, int n, int hb, int rb,
+                                   int t_lo, int t_hi, int slot, bool whole) {
+        b = __builtin_amdgcn_readfirstlane(b);
+        n = __builtin_amdgcn_readfirstlane(n);
+        hb = __builtin_amdgcn_readfirstlane(hb);
+        rb = __builtin_amdgcn_readfirstlane(rb);
+        t_lo = __builtin_amdgcn_readfirstlane(t_lo);
+        t_hi = __builtin_amdgcn_readfirstlane(t_hi);
+        slot = __builtin_amdgcn_readfirstlane(slot);
 
-        const int tok = t_lo + st * TPS + phiu * TPW + sg;
-        bool vis = row_ok && tok < t_hi;
-        if constexpr (CAUSAL) vis = vis && tok <= causal_last;
-        const float x = vis ? s * a.qscale : kNegInf;
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int hg = wave % HG;
+        const int ti = wave / HG;
+        const int sl = lane & (LPT - 1);
+        const int sg = lane >> LB;
+        const int hs = sg % HS;
+        const int ts = sg / HS;
+        const int hh = hg * HS + hs;                // head index inside the block
+        const int kvh = hb * HPW + hh;
+        const bool head_ok = kvh < a.Hkv;
 
-        const float mx = AllReduce<LB, 0, LOGU>::max(x);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float p = fast_exp2(x - m_use);
-        // alpha = 1 exactly when the row maximum did not move (also for rows
-        // that have seen nothing yet), so the rescale below can be skipped
-        const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_use);
-        const float psum = AllReduce<LB, 0, LOGU>::sum(p);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        const int row0 = rb * RB;
+        if (a.causal) {
+            // no row of this block sees a key past (last query position) + n - qLen
+            const int i_max = (min(row0 + RB, a.R) - 1) / a.G;
+            t_hi = min(t_hi, i_max + n - a.qLen + 1);
+        }
+        const int nsteps = t_hi > t_lo ? (t_hi - t_lo + TSTEP - 1) / TSTEP : 0;
 
-        wave_lds_sync();
-        lds_p[wave][sg][phi] = p;
-        lds_a[wave][sg][phir] = alpha;
-        wave_lds_sync();
-        float pc[N], ac[RB];
-#pragma unroll
-        for (int k = 0; k < N; ++k) pc[k] = lds_p[wave][sg][k];
-        bool moved = false;
+        // lane permutation of the reduce-scatter
+        const int gperm = sl ^ (((sl >> 2) & 1) * 3);
+        const int phi = gperm >> (LB - H);
+        const int phir = phi & (RB - 1);
+        const int phiu = phi >> LOGRB;
+
+        // the score this lane finishes with belongs to row (row0 + phir)
+        const int my_row = row0 + phir;
+        const bool row_ok = head_ok && my_row < a.R;
+        const int causal_last = a.causal ? my_row / a.G + n - a.qLen : INT32_MAX;
+
+        // Q rows of this lane's head, resident for the whole segment (16-bit)
+        u32x4 qr[RB];
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            ac[r] = lds_a[wave][sg][r];
-            moved |= ac[r] != 1.f;
-        }
-        if (__any(moved)) {
-#pragma unroll
-            for (int r = 0; r < RB; ++r)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[r][e] *= ac[r];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float vf[8];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) unpack2<DT>(vr[u][c], vf[2 * c], vf[2 * c + 1]);
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const float pr = pc[r + RB * u];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[r][e] = fmaf(pr, vf[e], o[r][e]);
+            const int row = row0 + (r ^ phir);
+            if (head_ok && row < a.R) {
+                const int i = row / a.G;
+                const int h = kvh * a.G + row % a.G;
+                const uint16_t *qp = (const uint16_t *)a.q +
+                                     (((size_t)b * a.qLen + i) * a.Hq + h) * D + 8 * sl;
+                qr[r] = *(const u32x4 *)qp;
+            } else {
+                qr[r] = u32x4{0, 0, 0, 0};
             }
         }
-    };
 
-    // K-outer loop: wave w takes steps w, w + 4, ...; loads of the next step
-    // are issued before the current one is computed (register double buffer).
-    {
-        u32x4 kA[U], vA[U], kB[U], vB[U];
-        int st = wave;
-        if (st < nsteps) load_step(st, kA, vA);
-        while (st < nsteps) {
-            if (st + kWaves < nsteps) load_step(st + kWaves, kB, vB);
-            compute_step(st, kA, vA);
-            st += kWaves;
-            if (st >= nsteps) break;
-            if (st + kWaves < nsteps) load_step(st + kWaves, kA, vA);
-            compute_step(st, kB, vB);
-            st += kWaves;
+        // K/V of sequence b through buffer descriptors whose range ends with
+        // token t_hi - 1: loads past the segment (the ragged end of the last
+        // step, the prefetch after the final step) return zeros without
+        // touching memory, so every load is issued unconditionally.  Lanes of
+        // a head past Hkv get an offset beyond any valid range (< 2^30).
+        const uint32_t tok_bytes = (uint32_t)a.Hkv * D * 2;
+        const size_t seq_off = (size_t)b * a.kv_cap * a.Hkv * D;
+        const uint32_t range = (uint32_t)t_hi * tok_bytes;
+        const __amdgpu_buffer_rsrc_t krsrc = make_rsrc((const uint16_t *)a.k + seq_off, range);
+        const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc((const uint16_t *)a.v + seq_off, range);
+        const uint32_t lane_base = head_ok ? (uint32_t)kvh * D * 2 + 16u * sl : 0x80000000u;
+        uint32_t koff[U], voff[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            koff[u] = lane_base + (uint32_t)((u ^ phiu) * TSUB + ts) * tok_bytes;
+            voff[u] = lane_base + (uint32_t)(u * TSUB + ts) * tok_bytes;
         }
-    }
 
-    // ---- epilogue: merge token slots, then waves, then write ----
-    wave_lds_sync();
-    if (phiu == 0) {
-        lds_ml[wave][sg][0][phir] = m_run;
-        lds_ml[wave][sg][1][phir] = l_run;
-    }
-    wave_lds_sync();
-    float wm[RB], wl[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        float M = kNegInf;
-#pragma unroll
-        for (int s2 = 0; s2 < TPW; ++s2) M = fmaxf(M, lds_ml[wave][s2][0][r]);
-        float L = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < TPW; ++s2) {
-            const float ms = lds_ml[wave][s2][0][r];
-            L += (ms == kNegInf ? 0.f : fast_exp2(ms - M)) * lds_ml[wave][s2][1][r];
-        }
-        const float mine = lds_ml[wave][sg][0][r];
-        const float sc = mine == kNegInf ? 0.f : fast_exp2(mine - M);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[r][e] *= sc;
-        wm[r] = M;
-        wl[r] = L;
-    }
-#pragma unroll
-    for (int x = LPT; x < 64; x <<= 1)
+        float m_run = kNegInf, l_run = 0.f;
+        float o[RB][8];
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[r][e] += __shfl_xor(o[r][e], x);
-    if (sg == 0) {
+            for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+
+        auto load_step = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[U]) {
+            const uint32_t base = (uint32_t)(t_lo + st * TSTEP) * tok_bytes;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                kr[u] = load16(krsrc, base + koff[u]);
+                vr[u] = load16(vrsrc, base + voff[u]);
+            }
+        };
+
+        auto compute_step = [&](int st, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
+            float v[N];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    float acc = 0.f;
+                    acc = dot2<DT>(qr[r][0], kr[u][0], acc);
+                    acc = dot2<DT>(qr[r][1], kr[u][1], acc);
+                    acc = dot2<DT>(qr[r][2], kr[u][2], acc);
+                    acc = dot2<DT>(qr[r][3], kr[u][3], acc);
+                    v[r + RB * u] = acc;
+                }
+            Halve<LB, N, 0, H>::run(v);
+            const float s = AllReduce<LB, H, LB>::sum(v[0]);
+
+            const int tok = t_lo + st * TSTEP + phiu * TSUB + ts;
+            const bool vis = row_ok && tok < t_hi && tok <= causal_last;
+            const float x = vis ? s * a.qscale : kNegInf;
+
+            const float mx = AllReduce<LB, 0, LOGU>::max(x);
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = m_new == kNegInf ? 0.f : m_new;
+            const float p = fast_exp2(x - m_use);
+            // alpha = 1 exactly when the row maximum did not move (also for
+            // rows that have seen nothing yet), so the rescale can be skipped
+            const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_use);
+            const float psum = AllReduce<LB, 0, LOGU>::sum(p);
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+
+            wave_lds_sync();
+            sm.p[wave][sg][phi] = p;
+            sm.a[wave][sg][phir] = alpha;
+            wave_lds_sync();
+            float pc[N], ac[RB];
+#pragma unroll
+            for (int k = 0; k < N; ++k) pc[k] = sm.p[wave][sg][k];
+            bool moved = false;
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                ac[r] = sm.a[wave][sg][r];
+                moved |= ac[r] != 1.f;
+            }
+            if (__any(moved)) {
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[r][e] *= ac[r];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float vf[8];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) unpack2<DT>(vr[u][c], vf[2 * c], vf[2 * c + 1]);
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    const float pr = pc[r + RB * u];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[r][e] = fmaf(pr, vf[e], o[r][e]);
+                }
+            }
+        };
+
+        // K-outer loop: the wave with token interleave ti takes steps ti,
+        // ti + TI, ...; the loads of its next step are issued before the
+        // current one is computed (register double buffer).  Loads are
+        // unconditional, so the wait counts stay exact.
+        {
+            const int nmine = nsteps > ti ? (nsteps - ti + TI - 1) / TI : 0;
+            u32x4 kA[U], vA[U], kB[U], vB[U];
+            int st = ti;
+            load_step(st, kA, vA);
+            for (int pair = 0; pair < nmine / 2; ++pair) {
+                load_step(st + TI, kB, vB);
+                compute_step(st, kA, vA);
+                load_step(st + 2 * TI, kA, vA);
+                compute_step(st + TI, kB, vB);
+                st += 2 * TI;
+            }
+            if (nmine & 1) compute_step(st, kA, vA);
+        }
+
+        // ---- merge the states of each (head, row), then write ----
+        const int state = ti * TSUB + ts;
+        if (phiu == 0) {
+            sm.m[state][hh][phir] = m_run;
+            sm.l[state][hh][phir] = l_run;
+        }
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) lds_o[wave][r][8 * sl + e] = o[r][e];
-    }
-    if (lane == 0) {
+            for (int e = 0; e < 8; e += 4)
+                *(f32x4 *)&sm.o[state][hh][r][8 * sl + e] =
+                    f32x4{o[r][e], o[r][e + 1], o[r][e + 2], o[r][e + 3]};
+        __syncthreads();
+
+        constexpr int Q4 = D / 4;
+        for (int idx = threadIdx.x; idx < HPW * RB * Q4; idx += kWaves * 64) {
+            const int d0 = (idx % Q4) * 4;
+            const int r = (idx / Q4) % RB;
+            const int hx = idx / (Q4 * RB);
+            const int row = row0 + r;
+            const int head = hb * HPW + hx;
+            if (row >= a.R || head >= a.Hkv) continue;
+            float M = kNegInf;
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            lds_wml[wave][0][r] = wm[r];
-            lds_wml[wave][1][r] = wl[r];
+            for (int s2 = 0; s2 < NSTATE; ++s2) M = fmaxf(M, sm.m[s2][hx][r]);
+            float num[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
+            if (M != kNegInf) {
+#pragma unroll
+                for (int s2 = 0; s2 < NSTATE; ++s2) {
+                    const float ms = sm.m[s2][hx][r];
+                    const float sc = ms == kNegInf ? 0.f : fast_exp2(ms - M);
+                    den += sc * sm.l[s2][hx][r];
+                    const f32x4 os = *(const f32x4 *)&sm.o[s2][hx][r][d0];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) num[j] += sc * os[j];
+                }
+            }
+            const bool empty = !(den > 0.f);
+            const float inv = empty ? 0.f : 1.f / den;
+            const float lse2 = empty ? kNegInf : M + fast_log2(den);
+            if (whole) {
+                const int i = row / a.G;
+                const int h = head * a.G + row % a.G;
+                uint16_t *op = (uint16_t *)a.out + (((size_t)b * a.qLen + i) * a.Hq + h) * D + d0;
+                *(u32x2 *)op = u32x2{pack2<DT>(num[0] * inv, num[1] * inv),
+                                     pack2<DT>(num[2] * inv, num[3] * inv)};
+                if (d0 == 0 && a.lse)
+                    a.lse[((size_t)b * a.Hq + h) * a.qLen + i] = empty ? kNegInf : lse2 * kLn2;
+            } else {
+                const size_t e = ((size_t)slot * HPW + hx) * RB + r;
+                *(f32x4 *)(a.ws_o + e * D + d0) =
+                    f32x4{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+                if (d0 == 0) a.ws_lse[e] = lse2;
+            }
         }
+        __syncthreads();    // the LDS state is reused by the next segment
     }
+};
+
+// Exclusive prefix sums of the clamped sequence lengths into cum[0..B]
+// (cum[B] = total), computed by the whole workgroup.
+__device__ void length_prefix_sums(const KernelArgs &a, long long *cum, long long *wave_tot) {
+    constexpr int PER = (kMaxBalancedBatch + kWaves * 64 - 1) / (kWaves * 64);
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    long long v[PER];
+    long long mine = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int bb = t * PER + j;
+        v[j] = bb < a.B ? clampi(a.seqlens ? a.seqlens[bb] : a.kv_cap, 0, a.kv_cap) : 0;
+        mine += v[j];
+    }
+    // inclusive scan of `mine` across the wave
+    long long inc = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const long long y = __shfl_up(inc, d);
+        if (lane >= d) inc += y;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
     __syncthreads();
+    long long before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_tot[w];
+    long long run = before + inc - mine;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int bb = t * PER + j;
+        if (bb < a.B) cum[bb] = run;
+        run += v[j];
+    }
+    if (t == kWaves * 64 - 1) cum[a.B] = run;     // the total (entries past B are 0)
+    __syncthreads();
+}
 
-    constexpr int Q4 = D / 4;
-    for (int idx = threadIdx.x; idx < RB * Q4; idx += kWaves * 64) {
-        const int r = idx / Q4;
-        const int d0 = (idx % Q4) * 4;
-        const int row = row0 + r;
-        if (row >= a.R) continue;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_wml[w][0][r]);
-        float num[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
-        if (M != kNegInf) {
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float mw = lds_wml[w][0][r];
-                const float sc = mw == kNegInf ? 0.f : fast_exp2(mw - M);
-                den += sc * lds_wml[w][1][r];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) num[j] += sc * lds_o[w][r][d0 + j];
-            }
+template <int DT, int D, int RB, int HS, int HG, int SCHED>
+__global__ __launch_bounds__(kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(MXFA_VALU_WAVES_PER_EU)))
+void split_kv_valu_kernel(KernelArgs a) {
+    using V = Valu<DT, D, RB, HS, HG>;
+    __shared__ __attribute__((aligned(16))) typename V::Smem sm;
+    const int HR = a.head_blocks * a.row_blocks;
+    if constexpr (SCHED == kFixed) {
+        const int split = blockIdx.x;
+        const int y = blockIdx.y;
+        const int b = blockIdx.z;
+        const int n = clampi(a.seqlens ? a.seqlens[b] : a.kv_cap, 0, a.kv_cap);
+        const int t_lo = split * a.chunk;
+        if (split > 0 && t_lo >= n) return;   // partition past this sequence
+        const int t_hi = min(t_lo + a.chunk, n);
+        const int slot = (b * HR + y) * a.S + split;
+        V::segment(a, sm, b, n, y / a.row_blocks, y % a.row_blocks, t_lo, t_hi, slot,
+                   t_lo == 0 && t_hi == n);
+    } else {
+        __shared__ long long cum[kMaxBalancedBatch + 1];
+        __shared__ long long wave_tot[kWaves];
+        length_prefix_sums(a, cum, wave_tot);
+        const long long T = cum[a.B] * HR;
+        long long W = (T + a.S - 1) / a.S;
+        if (W < a.min_share) W = a.min_share;
+        const int w = blockIdx.x;
+        if (w == 0) {
+            for (int bb = threadIdx.x; bb <= a.B; bb += kWaves * 64)
+                ((long long *)a.ws_cum)[bb] = cum[bb];
+            if (threadIdx.x == 0) ((long long *)a.ws_cum)[a.B + 1] = W;
         }
-        const bool empty = !(den > 0.f);
-        const float inv = empty ? 0.f : 1.f / den;
-        const float lse2 = empty ? kNegInf : M + fast_log2(den);
-        const int i = row / a.G;
-        const int h = kvh * a.G + row % a.G;
-        const size_t orow = ((size_t)b * a.Hq + h) * a.qLen + i;   // [B, Hq, qLen]
-        if (a.S == 1) {
-            uint16_t *op = (uint16_t *)a.out + (((size_t)b * a.qLen + i) * a.Hq + h) * D + d0;
-            *(u32x2 *)op = u32x2{pack2<DT>(num[0] * inv, num[1] * inv),
-                                 pack2<DT>(num[2] * inv, num[3] * inv)};
-            if (d0 == 0 && a.lse) a.lse[orow] = empty ? kNegInf : lse2 * kLn2;
-        } else {
-            float *wp = a.ws_o + (orow * a.S + split) * D + d0;
-            *(f32x4 *)wp = f32x4{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
-            if (d0 == 0) a.ws_lse[orow * a.S + split] = lse2;
+        long long g = (long long)w * W;
+        if (g >= T) return;
+        const long long gend = g + W < T ? g + W : T;
+        // sequence holding global token g: the last b with cum[b] * HR <= g
+        int lo = 0, hi = a.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cum[mid] * HR <= g) lo = mid; else hi = mid - 1;
+        }
+        int b = lo;
+        int n = (int)(cum[b + 1] - cum[b]);
+        const long long off = g - cum[b] * HR;
+        int j = (int)(off / n);
+        int t = (int)(off % n);
+        while (g < gend) {
+            const int seg = (int)((long long)(n - t) < gend - g ? (long long)(n - t) : gend - g);
+            V::segment(a, sm, b, n, j / a.row_blocks, j % a.row_blocks, t, t + seg,
+                       w + b * HR + j, t == 0 && seg == n);
+            g += seg;
+            t = 0;
+            if (++j == HR) {
+                j = 0;
+                do { ++b; } while (b < a.B && cum[b + 1] == cum[b]);
+                if (b >= a.B) break;
+                n = (int)(cum[b + 1] - cum[b]);
+            }
         }
     }
 }
 
-template <int DT, int D, int RB, bool CAUSAL>
-hipError_t launch_t(const SplitArgs &a, dim3 grid, hipStream_t stream) {
-    SplitArgs args = a;
+template <int DT, int D, int RB, int HS, int HG>
+hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
+    KernelArgs args = a;
     void *kargs[] = {&args};
-    return hipLaunchKernel((const void *)&split_kv_valu_kernel<DT, D, RB, CAUSAL>, grid,
-                           dim3(kWaves * 64), kargs, 0, stream);
+    const void *fn = a.schedule == kBalanced
+        ? (const void *)&split_kv_valu_kernel<DT, D, RB, HS, HG, kBalanced>
+        : (const void *)&split_kv_valu_kernel<DT, D, RB, HS, HG, kFixed>;
+    return hipLaunchKernel(fn, grid, dim3(kWaves * 64), kargs, 0, stream);
 }
 
+// Head layouts: all slots are heads with 2 or 1 head groups per workgroup,
+// or one head per workgroup with the slots on different tokens.
 template <int DT, int D, int RB>
-hipError_t launch_c(const SplitArgs &a, int causal, dim3 grid, hipStream_t stream) {
-    return causal ? launch_t<DT, D, RB, true>(a, grid, stream)
-                  : launch_t<DT, D, RB, false>(a, grid, stream);
+hipError_t launch_h(const KernelArgs &a, int layout, dim3 grid, hipStream_t stream) {
+    constexpr int TPW = 64 / (D / 8);
+    switch (layout) {
+    case kHeadsX2: return launch_t<DT, D, RB, TPW, 2>(a, grid, stream);
+    case kHeadsX1: return launch_t<DT, D, RB, TPW, 1>(a, grid, stream);
+    case kTokens: return launch_t<DT, D, RB, 1, 1>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int DT, int D>
-hipError_t launch_rb(const SplitArgs &a, int rb, int causal, dim3 grid, hipStream_t stream) {
-    switch (rb) {
-    case 1: return launch_c<DT, D, 1>(a, causal, grid, stream);
-    case 2: return launch_c<DT, D, 2>(a, causal, grid, stream);
-    case 4: return launch_c<DT, D, 4>(a, causal, grid, stream);
-    case 8: return launch_c<DT, D, 8>(a, causal, grid, stream);
+hipError_t launch_rb(const KernelArgs &a, int layout, dim3 grid, hipStream_t stream) {
+    switch (a.row_block) {
+    case 1: return launch_h<DT, D, 1>(a, layout, grid, stream);
+    case 2: return launch_h<DT, D, 2>(a, layout, grid, stream);
+    case 4: return launch_h<DT, D, 4>(a, layout, grid, stream);
+    case 8: return launch_h<DT, D, 8>(a, layout, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_split_valu(const SplitArgs &a, int dtype, int D, int row_block,
-                             int causal, dim3 grid, hipStream_t stream) {
+hipError_t launch_split_valu(const KernelArgs &a, int dtype, int layout, dim3 grid,
+                             hipStream_t stream) {
     if (dtype == kFp16) {
-        if (D == 128) return launch_rb<kFp16, 128>(a, row_block, causal, grid, stream);
-        if (D == 64) return launch_rb<kFp16, 64>(a, row_block, causal, grid, stream);
+        if (a.D == 128) return launch_rb<kFp16, 128>(a, layout, grid, stream);
+        if (a.D == 64) return launch_rb<kFp16, 64>(a, layout, grid, stream);
     } else {
-        if (D == 128) return launch_rb<kBf16, 128>(a, row_block, causal, grid, stream);
-        if (D == 64) return launch_rb<kBf16, 64>(a, row_block, causal, grid, stream);
+        if (a.D == 128) return launch_rb<kBf16, 128>(a, layout, grid, stream);
+        if (a.D == 64) return launch_rb<kBf16, 64>(a, layout, grid, stream);
     }
     return hipErrorInvalidValue;
 }

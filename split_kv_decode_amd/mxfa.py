@@ -25,8 +25,10 @@ EXPORTS = ("mxfa_fwd_kvcache", "mxfa_fwd_kvcache_ws", "mxfa_workspace_size",
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int), ("rows", ctypes.c_int),
-                ("row_block", ctypes.c_int), ("num_splits", ctypes.c_int),
+    _fields_ = [("path", ctypes.c_int), ("layout", ctypes.c_int), ("schedule", ctypes.c_int),
+                ("rows", ctypes.c_int),
+                ("row_block", ctypes.c_int), ("head_block", ctypes.c_int),
+                ("num_splits", ctypes.c_int),
                 ("chunk", ctypes.c_int), ("grid_x", ctypes.c_int),
                 ("grid_y", ctypes.c_int), ("grid_z", ctypes.c_int),
                 ("combine", ctypes.c_int), ("num_cus", ctypes.c_int),

@@ -142,21 +142,38 @@ SHAPES = [
 def test_plan_covers_the_cache_exactly(shape, num_splits):
     B, Hq, Hkv, D, qLen, cap, causal, dt = shape
     p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits)
+    assert p.rows == (Hq // Hkv) * qLen
+    assert p.row_block in (1, 2, 4, 8) and p.row_block >= min(p.rows, 8)
+    assert p.head_block in (1, 4, 8, 16) and Hkv % p.head_block == 0
+    streams = B * (Hkv // p.head_block) * -(-p.rows // p.row_block)
+    entry = p.head_block * p.row_block * (D + 1) * 4
+    if p.schedule == 1:                      # balanced: planner's own choice only
+        assert num_splits == 0 and p.combine == 1 and p.chunk == 0
+        assert (p.grid_x, p.grid_y, p.grid_z) == (p.num_splits, 1, 1)
+        assert p.workspace_bytes >= (p.num_splits + streams) * entry + (B + 2) * 8
+        return
     S, C = p.num_splits, p.chunk
     assert S >= 1 and C >= 1
     if cap > 0:
         assert (S - 1) * C < cap <= S * C          # every partition non-empty at kv_cap
         if num_splits:
             assert S <= min(num_splits, cap)
-    assert p.rows == (Hq // Hkv) * qLen
-    assert p.row_block in (1, 2, 4, 8) and p.row_block >= min(p.rows, 8)
     assert p.grid_x == S and p.grid_z == B
-    assert p.grid_y == Hkv * -(-p.rows // p.row_block)
+    assert p.grid_y == (Hkv // p.head_block) * -(-p.rows // p.row_block)
     assert p.combine == (1 if S > 1 else 0)
     if S > 1:
-        assert p.workspace_bytes >= B * Hq * qLen * S * (D + 1) * 4
+        assert p.workspace_bytes >= streams * S * entry
     else:
         assert p.workspace_bytes == 0
+
+
+def test_balanced_schedule_is_chosen_for_long_ragged_batches():
+    p = m.plan(64, 32, 8, 128, 1, 16384, 0, 1, 0, 256)
+    assert p.schedule == 1 and p.grid_x == 512
+    p = m.plan(64, 32, 8, 128, 1, 16384, 0, 1, 16, 256)
+    assert p.schedule == 0 and p.num_splits == 16
+    p = m.plan(2000, 32, 8, 128, 1, 4096, 0, 1, 0, 256)     # batch past the LDS table
+    assert p.schedule == 0
 
 
 def test_plan_fills_the_chip_at_low_batch():
