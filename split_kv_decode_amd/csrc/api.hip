@@ -126,12 +126,19 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     const int G = p.Hq / p.Hkv;
     const long long R = (long long)G * p.qLen;
     if (R > INT32_MAX) return MXFA_ERR_UNSUPPORTED;
-    pl.path = MXFA_PATH_VALU;
     pl.rows = (int)R;
-    pl.row_block = next_pow2_le8((int)R);
-    const int row_blocks = R > 0 ? ceil_div(R, pl.row_block) : 1;
     int hpb = 1;
-    pl.layout = valu_layout(p.Hkv, p.D, &hpb);
+    if (R >= kMfmaMinRows) {
+        // many rows per kv head: Q K^T and P V are dense 16-row tiles
+        pl.path = MXFA_PATH_MFMA;
+        pl.row_block = kMfmaRowBlock;
+        pl.layout = kTokens;
+    } else {
+        pl.path = MXFA_PATH_VALU;
+        pl.row_block = next_pow2_le8((int)R);
+        pl.layout = valu_layout(p.Hkv, p.D, &hpb);
+    }
+    const int row_blocks = R > 0 ? ceil_div(R, pl.row_block) : 1;
     pl.head_block = hpb;
     const int head_blocks = ceil_div(p.Hkv, hpb);
     if ((long long)head_blocks * row_blocks > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
@@ -252,7 +259,10 @@ mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seql
     a.qscale = (float)(1.4426950408889634 / std::sqrt((double)p.D));
     const dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z);
     if (t_ev_before && hipEventRecord(t_ev_before, stream) != hipSuccess) return MXFA_ERR_HIP;
-    if (launch_split_valu(a, p.dtype, pl.layout, grid, stream) != hipSuccess) return MXFA_ERR_HIP;
+    const hipError_t e = pl.path == MXFA_PATH_MFMA
+                             ? launch_split_mfma(a, p.dtype, grid, stream)
+                             : launch_split_valu(a, p.dtype, pl.layout, grid, stream);
+    if (e != hipSuccess) return MXFA_ERR_HIP;
     if (t_ev_after && hipEventRecord(t_ev_after, stream) != hipSuccess) return MXFA_ERR_HIP;
     if (pl.combine && launch_combine(a, p.dtype, stream) != hipSuccess) return MXFA_ERR_HIP;
     return MXFA_OK;

@@ -61,6 +61,13 @@ constexpr int kMaxBalancedBatch = 1024;
 hipError_t launch_split_valu(const KernelArgs &a, int dtype, int layout, dim3 grid,
                              hipStream_t stream);
 
+// Matrix-core split kernel: row_block must be 64 and head_block 1.
+hipError_t launch_split_mfma(const KernelArgs &a, int dtype, dim3 grid, hipStream_t stream);
+
 hipError_t launch_combine(const KernelArgs &a, int dtype, hipStream_t stream);
+
+// Query rows per kv head from which the matrix-core path is used.
+constexpr int kMfmaMinRows = 32;
+constexpr int kMfmaRowBlock = 64;
 
 }  // namespace mxfa

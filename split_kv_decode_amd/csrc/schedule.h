@@ -1,0 +1,131 @@
+// Work schedules shared by the split kernels (device code).
+//
+// A "stream" is the KV token range [0, n_b) of one (sequence b, head block,
+// row block); see launch.h.  drive_schedule hands a kernel's workgroup its
+// segments, each as (b, n_b, head block, row block, t_lo, t_hi, slot, whole):
+//   kFixed:    grid (S, head_blocks * row_blocks, B); one segment
+//              [split * chunk, (split + 1) * chunk) per workgroup, slot
+//              st * S + split.
+//   kBalanced: grid (P); the streams are laid end to end and workgroup w
+//              takes [w * W, (w + 1) * W) of the concatenation, W = max(
+//              ceil(total / P), min_share), as one segment per stream it
+//              touches, slot w + st.
+// `whole` marks a segment that is its stream's entire range; the kernel then
+// writes the final output instead of a partial.  The valid lengths live on
+// the device, so in the balanced schedule every workgroup first forms their
+// prefix sums (workgroup 0 also stores them, and W, for the merge kernel).
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxfa {
+
+constexpr int kScheduleThreads = 256;
+
+// Workgroup-uniform values read from LDS are otherwise held in vector
+// registers; readfirstlane moves them to scalar registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ long long uni(long long x) {
+    const int lo = __builtin_amdgcn_readfirstlane((int)(x & 0xffffffff));
+    const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
+    return ((long long)hi << 32) | (unsigned)lo;
+}
+
+// Exclusive prefix sums of the clamped sequence lengths into cum[0..B]
+// (cum[B] = total), computed by the whole workgroup of 256 threads.
+__device__ __forceinline__ void length_prefix_sums(const KernelArgs &a, long long *cum,
+                                          long long *wave_tot) {
+    constexpr int PER = (kMaxBalancedBatch + kScheduleThreads - 1) / kScheduleThreads;
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    long long v[PER];
+    long long mine = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int bb = t * PER + j;
+        v[j] = bb < a.B ? clampi(a.seqlens ? a.seqlens[bb] : a.kv_cap, 0, a.kv_cap) : 0;
+        mine += v[j];
+    }
+    // inclusive scan of `mine` across the wave
+    long long inc = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const long long y = __shfl_up(inc, d);
+        if (lane >= d) inc += y;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    long long before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_tot[w];
+    long long run = before + inc - mine;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int bb = t * PER + j;
+        if (bb < a.B) cum[bb] = run;
+        run += v[j];
+    }
+    if (t == kScheduleThreads - 1) cum[a.B] = run;     // the total (entries past B are 0)
+    __syncthreads();
+}
+
+template <int SCHED, class Segment>
+__device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&segment) {
+    const int HR = a.head_blocks * a.row_blocks;
+    if constexpr (SCHED == kFixed) {
+        const int split = blockIdx.x;
+        const int y = blockIdx.y;
+        const int b = blockIdx.z;
+        const int n = clampi(a.seqlens ? a.seqlens[b] : a.kv_cap, 0, a.kv_cap);
+        const int t_lo = split * a.chunk;
+        if (split > 0 && t_lo >= n) return;   // partition past this sequence
+        const int t_hi = min(t_lo + a.chunk, n);
+        const int slot = (b * HR + y) * a.S + split;
+        segment(b, n, y / a.row_blocks, y % a.row_blocks, t_lo, t_hi, slot,
+                t_lo == 0 && t_hi == n);
+    } else {
+        __shared__ long long cum[kMaxBalancedBatch + 1];
+        __shared__ long long wave_tot[kScheduleThreads / 64];
+        length_prefix_sums(a, cum, wave_tot);
+        const long long T = uni(cum[a.B] * HR);
+        long long W = (T + a.S - 1) / a.S;
+        if (W < a.min_share) W = a.min_share;
+        W = uni(W);
+        const int w = blockIdx.x;
+        if (w == 0) {
+            for (int bb = threadIdx.x; bb <= a.B; bb += kScheduleThreads)
+                ((long long *)a.ws_cum)[bb] = cum[bb];
+            if (threadIdx.x == 0) ((long long *)a.ws_cum)[a.B + 1] = W;
+        }
+        long long g = (long long)w * W;
+        if (g >= T) return;
+        const long long gend = g + W < T ? g + W : T;
+        // sequence holding global token g: the last b with cum[b] * HR <= g
+        int lo = 0, hi = a.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cum[mid] * HR <= g) lo = mid; else hi = mid - 1;
+        }
+        int b = uni(lo);
+        int n = uni((int)(cum[b + 1] - cum[b]));
+        const long long off = uni(g - cum[b] * HR);
+        int j = uni((int)(off / n));
+        int t = uni((int)(off % n));
+        while (g < gend) {
+            const int seg = (int)((long long)(n - t) < gend - g ? (long long)(n - t) : gend - g);
+            segment(b, n, j / a.row_blocks, j % a.row_blocks, t, t + seg, (int)(w + b * HR + j),
+                    t == 0 && seg == n);
+            g += seg;
+            t = 0;
+            if (++j == HR) {
+                j = 0;
+                do { ++b; } while (b < a.B && cum[b + 1] == cum[b]);
+                b = uni(b);
+                if (b >= a.B) break;
+                n = uni((int)(cum[b + 1] - cum[b]));
+            }
+        }
+    }
+}
+
+}  // namespace mxfa

@@ -60,6 +60,7 @@
 // read on the device, so each workgroup first forms their prefix sums.
 #include "device_common.h"
 #include "launch.h"
+#include "schedule.h"
 
 namespace mxfa {
 namespace {
@@ -141,7 +142,7 @@ struct Valu {
     // Tokens [t_lo, t_hi) of the stream (b, hb, rb); n is sequence b's valid
     // length.  whole: the segment is the stream's entire range [0, n), so the
     // final output is written; otherwise the partial goes to `slot`.
-    __device__ static void segment(const KernelArgs &a, Smem &sm, int b, int n, int hb, int rb,
+    __device__ static __forceinline__ void segment(const KernelArgs &a, Smem &sm, int b, int n, int hb, int rb,
                                    int t_lo, int t_hi, int slot, bool whole) {
         b = __builtin_amdgcn_readfirstlane(b);
         n = __builtin_amdgcn_readfirstlane(n);
@@ -374,101 +375,16 @@ struct Valu {
     }
 };
 
-// Exclusive prefix sums of the clamped sequence lengths into cum[0..B]
-// (cum[B] = total), computed by the whole workgroup.
-__device__ void length_prefix_sums(const KernelArgs &a, long long *cum, long long *wave_tot) {
-    constexpr int PER = (kMaxBalancedBatch + kWaves * 64 - 1) / (kWaves * 64);
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    long long v[PER];
-    long long mine = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int bb = t * PER + j;
-        v[j] = bb < a.B ? clampi(a.seqlens ? a.seqlens[bb] : a.kv_cap, 0, a.kv_cap) : 0;
-        mine += v[j];
-    }
-    // inclusive scan of `mine` across the wave
-    long long inc = mine;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const long long y = __shfl_up(inc, d);
-        if (lane >= d) inc += y;
-    }
-    if (lane == 63) wave_tot[wave] = inc;
-    __syncthreads();
-    long long before = 0;
-    for (int w = 0; w < wave; ++w) before += wave_tot[w];
-    long long run = before + inc - mine;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int bb = t * PER + j;
-        if (bb < a.B) cum[bb] = run;
-        run += v[j];
-    }
-    if (t == kWaves * 64 - 1) cum[a.B] = run;     // the total (entries past B are 0)
-    __syncthreads();
-}
-
 template <int DT, int D, int RB, int HS, int HG, int SCHED>
 __global__ __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(MXFA_VALU_WAVES_PER_EU)))
 void split_kv_valu_kernel(KernelArgs a) {
     using V = Valu<DT, D, RB, HS, HG>;
     __shared__ __attribute__((aligned(16))) typename V::Smem sm;
-    const int HR = a.head_blocks * a.row_blocks;
-    if constexpr (SCHED == kFixed) {
-        const int split = blockIdx.x;
-        const int y = blockIdx.y;
-        const int b = blockIdx.z;
-        const int n = clampi(a.seqlens ? a.seqlens[b] : a.kv_cap, 0, a.kv_cap);
-        const int t_lo = split * a.chunk;
-        if (split > 0 && t_lo >= n) return;   // partition past this sequence
-        const int t_hi = min(t_lo + a.chunk, n);
-        const int slot = (b * HR + y) * a.S + split;
-        V::segment(a, sm, b, n, y / a.row_blocks, y % a.row_blocks, t_lo, t_hi, slot,
-                   t_lo == 0 && t_hi == n);
-    } else {
-        __shared__ long long cum[kMaxBalancedBatch + 1];
-        __shared__ long long wave_tot[kWaves];
-        length_prefix_sums(a, cum, wave_tot);
-        const long long T = cum[a.B] * HR;
-        long long W = (T + a.S - 1) / a.S;
-        if (W < a.min_share) W = a.min_share;
-        const int w = blockIdx.x;
-        if (w == 0) {
-            for (int bb = threadIdx.x; bb <= a.B; bb += kWaves * 64)
-                ((long long *)a.ws_cum)[bb] = cum[bb];
-            if (threadIdx.x == 0) ((long long *)a.ws_cum)[a.B + 1] = W;
-        }
-        long long g = (long long)w * W;
-        if (g >= T) return;
-        const long long gend = g + W < T ? g + W : T;
-        // sequence holding global token g: the last b with cum[b] * HR <= g
-        int lo = 0, hi = a.B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cum[mid] * HR <= g) lo = mid; else hi = mid - 1;
-        }
-        int b = lo;
-        int n = (int)(cum[b + 1] - cum[b]);
-        const long long off = g - cum[b] * HR;
-        int j = (int)(off / n);
-        int t = (int)(off % n);
-        while (g < gend) {
-            const int seg = (int)((long long)(n - t) < gend - g ? (long long)(n - t) : gend - g);
-            V::segment(a, sm, b, n, j / a.row_blocks, j % a.row_blocks, t, t + seg,
-                       w + b * HR + j, t == 0 && seg == n);
-            g += seg;
-            t = 0;
-            if (++j == HR) {
-                j = 0;
-                do { ++b; } while (b < a.B && cum[b + 1] == cum[b]);
-                if (b >= a.B) break;
-                n = (int)(cum[b + 1] - cum[b]);
-            }
-        }
-    }
+    drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
+                                 bool whole) {
+        V::segment(a, sm, b, n, hb, rb, t_lo, t_hi, slot, whole);
+    });
 }
 
 template <int DT, int D, int RB, int HS, int HG>

@@ -143,7 +143,10 @@ def test_plan_covers_the_cache_exactly(shape, num_splits):
     B, Hq, Hkv, D, qLen, cap, causal, dt = shape
     p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits)
     assert p.rows == (Hq // Hkv) * qLen
-    assert p.row_block in (1, 2, 4, 8) and p.row_block >= min(p.rows, 8)
+    if p.rows >= 32:
+        assert p.path == 1 and p.row_block == 64 and p.head_block == 1
+    else:
+        assert p.path == 0 and p.row_block in (1, 2, 4, 8) and p.row_block >= min(p.rows, 8)
     assert p.head_block in (1, 4, 8, 16) and Hkv % p.head_block == 0
     streams = B * (Hkv // p.head_block) * -(-p.rows // p.row_block)
     entry = p.head_block * p.row_block * (D + 1) * 4
