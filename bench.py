@@ -32,7 +32,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "qwen3_8b_decode"
 KERNEL_SOURCES = ["split_kv_decode_amd/csrc/split_valu.hip",
-                  "split_kv_decode_amd/csrc/device_common.h"]
+                  "split_kv_decode_amd/csrc/split_mfma.hip",
+                  "split_kv_decode_amd/csrc/schedule.h",
+                  "split_kv_decode_amd/csrc/device_common.h",
+                  "split_kv_decode_amd/csrc/launch.h"]
+SPLIT_KERNEL = {"valu": "split_kv_valu_kernel", "mfma": "split_kv_mfma_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -57,6 +61,91 @@ def traffic_for(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def _kernel_rows(csv_path):
+    import csv
+    with open(csv_path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands):
+    """Turn rocprofv3 outputs (kernel-trace stats, FETCH_SIZE pass, WRITE_SIZE
+    pass, each of a bench run with --copy-calibration) into a short summary
+    under profiles/ and the per-launch traffic record bench.py reports.
+    The counters are scaled by what they read for the 1 GiB device copy."""
+    import statistics
+    stats = _kernel_rows(os.path.join(trace_dir, "run_kernel_stats.csv"))
+    fetch = _kernel_rows(os.path.join(fetch_dir, "run_counter_collection.csv"))
+    write = _kernel_rows(os.path.join(write_dir, "run_counter_collection.csv"))
+    copy_bytes = float(1 << 30)
+
+    def per_kernel(rows, counter):
+        out = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return out
+
+    f_by, w_by = per_kernel(fetch, "FETCH_SIZE"), per_kernel(write, "WRITE_SIZE")
+    copy_name = [k for k in f_by if "copyBuffer" in k or "copy" in k.lower()]
+    big = lambda xs: [x for x in xs if x > copy_bytes / 4]
+    f_copy = statistics.median(big(f_by[copy_name[0]]))
+    w_copy = statistics.median(big(w_by[copy_name[0]]))
+    f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
+    split = [k for k in f_by if "split_kv_" in k][0]
+    merge = [k for k in f_by if "combine_kernel" in k]
+    f_split = statistics.median(f_by[split]) * f_scale
+    w_split = statistics.median(w_by[split]) * w_scale
+
+    import workloads as wl
+    w = wl.WORKLOADS[workload]
+    lens = wl.make_inputs(w).lengths() if w.len_range else [w.kv_cap] * w.B
+    alg = wl.kv_bytes(w, lens) + w.B * w.qLen * w.Hq * w.D * w.elt
+    kname = "split_kv_mfma_kernel" if "mfma" in split else "split_kv_valu_kernel"
+    trace_rows = [r for r in stats if "split_kv_" in r["Name"] or "combine_kernel" in r["Name"]]
+    lines = [f"# {kname} on {workload}", "",
+             f"Workload: {w.describe()}.", "",
+             "Commands (run from the repository root on one MI355X, after "
+             "`cd /tmp && export TMPDIR=/tmp`):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in trace_rows:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    avg_ns = float([r for r in trace_rows if "split_kv_" in r["Name"]][0]["AverageNs"])
+    lines += ["", "## HBM traffic per split-kernel launch (rocprofv3 --pmc)", "",
+              f"- copy calibration: a 1 GiB device copy reads as {f_copy / 2**20:.1f} MiB of "
+              f"FETCH_SIZE and {w_copy / 2**20:.1f} MiB of WRITE_SIZE; scale factors "
+              f"{f_scale:.3f} (fetch) and {w_scale:.3f} (write)",
+              f"- split kernel: fetch {f_split / 1e9:.4f} GB, write {w_split / 1e9:.4f} GB "
+              f"(scaled medians over {len(f_by[split])} launches)",
+              f"- algorithmic bytes per launch (K/V rows read once + Q): {alg / 1e9:.4f} GB; "
+              f"fetched / algorithmic = {f_split / alg:.4f}",
+              f"- achieved from the trace average: {alg / (avg_ns * 1e-9) / 1e9:.1f} GB/s "
+              f"({100 * alg / (avg_ns * 1e-9) / 1e9 / HBM_PEAK_GBS:.1f}% of 8 TB/s)"]
+    if merge:
+        fm = statistics.median(f_by[merge[0]]) * f_scale
+        wm = statistics.median(w_by[merge[0]]) * w_scale
+        lines.append(f"- merge kernel: fetch {fm / 1e6:.2f} MB, write {wm / 1e6:.2f} MB per launch")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    path = os.path.join(ROOT, "profiles", f"{kname}_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[workload] = {"kernel": kname, "kernel_digest": kernel_digest(),
+                     "bytes_per_launch": int(round(f_split + w_split)),
+                     "fetch_bytes": int(round(f_split)), "write_bytes": int(round(w_split)),
+                     "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(path)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -68,11 +157,18 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"),
+                    help="summarize rocprofv3 output directories into profiles/ (no GPU)")
+    ap.add_argument("--profile-command", action="append", default=[],
+                    help="command line recorded in the profile summary")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, args.workload, args.profile_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the split-KV path shards by batch or kv head with no exchange; see DESIGN.md)",
@@ -184,7 +280,7 @@ def main():
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "attn_calls_per_s": round(1e3 / ms_per_step, 1),
         "plan": plan,
-        "roofline": {"bound": "hbm", "kernel": "split_kv_valu_kernel",
+        "roofline": {"bound": "hbm", "kernel": SPLIT_KERNEL[plan["path"]],
                      "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(split_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
