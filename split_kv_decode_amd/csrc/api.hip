@@ -51,8 +51,11 @@ mxfa_status check_problem(const Problem &p) {
         return MXFA_ERR_INVALID_ARG;
     if (p.D != 64 && p.D != 128) return MXFA_ERR_UNSUPPORTED;
     if (p.B > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
-    // K/V are addressed with 32-bit byte offsets inside one sequence
+    // K/V are addressed with 32-bit byte offsets inside one sequence; loads
+    // issued ahead may run up to 1024 tokens past the cache, so both the
+    // cache and that slack must stay below 2^30 bytes
     if ((uint64_t)p.kv_cap * p.Hkv * p.D * 2 > (UINT64_C(1) << 30)) return MXFA_ERR_UNSUPPORTED;
+    if ((uint64_t)1024 * p.Hkv * p.D * 2 > (UINT64_C(1) << 30)) return MXFA_ERR_UNSUPPORTED;
     return MXFA_OK;
 }
 
@@ -99,7 +102,8 @@ int valu_layout(int Hkv, int D, int *heads_per_block) {
 //   full length, but no shorter than a floor that keeps the partial results
 //   (row_block x (D + 1) floats per head, written once, read once by the
 //   merge) a small fraction of the partition's K/V bytes.
-//   Balanced: a fixed grid of kBalancedPerCU workgroups per CU, each taking
+//   Balanced: a fixed grid of as many workgroups as are resident at once
+//   (two per CU for the VALU kernel, one for the matrix-core kernel), each taking
 //   an equal share (at least the same floor) of all streams laid end to end,
 //   so ragged batches keep every workgroup equally busy.
 // The balanced schedule is used when the planner is free to choose
@@ -119,7 +123,10 @@ size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *fp) {
     constexpr int kChunkAlign = 64;
     constexpr int kTargetPerCU = 8;
-    constexpr int kBalancedPerCU = 2;
+    // workgroups resident per CU: the VALU kernel runs two, the matrix-core
+    // kernel one (its LDS and registers fill the CU)
+    constexpr int kValuPerCU = 2;
+    constexpr int kMfmaPerCU = 1;
     mxfa_plan_t pl;
     std::memset(&pl, 0, sizeof(pl));
     if (num_cus <= 0) num_cus = kDefaultCUs;
@@ -168,7 +175,7 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     long long slots;
     if (num_splits == 0 && S > 1 && p.B <= kMaxBalancedBatch) {
         pl.schedule = kBalanced;
-        const int P = num_cus * kBalancedPerCU;
+        const int P = num_cus * (pl.path == MXFA_PATH_MFMA ? kMfmaPerCU : kValuPerCU);
         pl.num_splits = P;
         pl.chunk = 0;
         pl.grid_x = P;

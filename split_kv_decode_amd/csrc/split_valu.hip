@@ -169,6 +169,7 @@ struct Valu {
             // no row of this block sees a key past (last query position) + n - qLen
             const int i_max = (min(row0 + RB, a.R) - 1) / a.G;
             t_hi = min(t_hi, i_max + n - a.qLen + 1);
+            t_hi = max(t_hi, t_lo);     // an empty segment, never a negative range
         }
         const int nsteps = t_hi > t_lo ? (t_hi - t_lo + TSTEP - 1) / TSTEP : 0;
 

@@ -94,6 +94,8 @@ INV, UNS = mxfa.MXFA_ERR_INVALID_ARG, mxfa.MXFA_ERR_UNSUPPORTED
     (dict(causal=2), INV), (dict(causal=-1), INV), (dict(dtype=2), INV), (dict(dtype=-1), INV),
     (dict(B=2**30, cap=2**30), INV),                       # byte size overflow
     (dict(D=96), UNS), (dict(D=256), UNS), (dict(D=32), UNS), (dict(B=70000), UNS),
+    (dict(cap=2**16, Hq=128, Hkv=128), UNS),               # cache past 2^30 bytes per sequence
+    (dict(cap=1, Hq=8192, Hkv=8192), UNS),                 # 1024-token slack past 2^30 bytes
 ])
 def test_invalid_arguments_rejected_before_any_hip_call(kw, status):
     assert _call(**kw) == status
@@ -177,6 +179,14 @@ def test_balanced_schedule_is_chosen_for_long_ragged_batches():
     assert p.schedule == 0 and p.num_splits == 16
     p = m.plan(2000, 32, 8, 128, 1, 4096, 0, 1, 0, 256)     # batch past the LDS table
     assert p.schedule == 0
+
+
+def test_balanced_grid_is_one_resident_wave_of_workgroups():
+    # VALU kernel: two workgroups per CU; matrix-core kernel: one per CU
+    assert m.plan(64, 32, 8, 128, 1, 16384, 0, 1, 0, 256).grid_x == 512
+    p = m.plan(4, 64, 8, 128, 8, 32768, 1, 1, 0, 256)
+    assert p.path == 1 and p.schedule == 1 and p.grid_x == 256
+    assert m.plan(4, 64, 8, 128, 8, 32768, 1, 1, 0, 80).grid_x == 80
 
 
 def test_plan_fills_the_chip_at_low_batch():

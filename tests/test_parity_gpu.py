@@ -115,7 +115,7 @@ def test_deterministic_run_to_run():
 @pytest.mark.parametrize("G,qLen,causal", [(1, 1, False), (2, 1, False), (4, 1, False),
                                           (8, 1, False), (1, 3, True), (3, 1, False),
                                           (5, 2, True), (4, 4, True), (8, 8, True),
-                                          (16, 2, False)])
+                                          (16, 2, False), (16, 8, True)])
 def test_shape_sweep(D, dtype, G, qLen, causal):
     Hkv = 2
     w = wl.Workload("sweep", B=2, qLen=qLen, Hq=G * Hkv, Hkv=Hkv, D=D, kv_cap=1100,
@@ -151,6 +151,23 @@ def test_empty_rows_and_zero_lengths():
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
     assert np.all(np.isneginf(lse[1][:, :2]))           # rows 0,1 see nothing with n=2
     for ns in (1, 5):
+        _full_check(inp, num_splits=ns)
+
+
+@pytest.mark.parametrize("G,qLen,Hkv,D,cap,lengths", [
+    (4, 4, 2, 64, 3, [0, 1, 3]),          # VALU path, two row blocks of 8
+    (8, 16, 1, 128, 5, [0, 2, 5]),        # matrix-core path, two row blocks of 64
+])
+def test_causal_draft_longer_than_the_cache(G, qLen, Hkv, D, cap, lengths):
+    # rows whose causal bound lies before the first key see nothing; whole
+    # row blocks can be empty while the sequence is not
+    w = wl.Workload("draft", B=len(lengths), qLen=qLen, Hq=G * Hkv, Hkv=Hkv, D=D,
+                    kv_cap=cap, dtype="bf16", causal=True, sigma=1.0, seed=77,
+                    len_range=(0, cap))
+    inp = wl.make_inputs(w, lengths=lengths)
+    out, lse, _ = _full_check(inp)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    for ns in (1, 3):
         _full_check(inp, num_splits=ns)
 
 
