@@ -153,6 +153,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="run on a paged copy of the cache with this page size "
+                         "(0 = the contiguous cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -186,22 +189,37 @@ def main():
     t0 = time.time()
     inp = wl.make_inputs(w)
     lens = inp.lengths()
-    g = inp.to(dev)
-    print(f"# inputs {w.name} ({w.describe()}) generated in {time.time() - t0:.1f}s",
-          file=sys.stderr, flush=True)
+    P = args.page_size
+    paged_cpu = wl.to_paged(inp, P) if P else None
+    paged = paged_cpu.to(dev) if P else None
+    g = inp.to(dev) if not P else None
+    q = inp.q.to(dev)
+    print(f"# inputs {w.name} ({w.describe()}{f', pages of {P}' if P else ''}) "
+          f"generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     dt = mx.MXFA_BF16 if w.dtype == "bf16" else mx.MXFA_FP16
-    need = mx.workspace_size(w.B, w.Hq, w.Hkv, w.D, w.qLen, w.kv_cap, w.causal, dt,
-                             args.num_splits)
+    if P:
+        need = mx.workspace_size_paged(w.B, w.Hq, w.Hkv, w.D, w.qLen, P,
+                                       paged.block_table.shape[1], w.causal, dt,
+                                       args.num_splits)
+    else:
+        need = mx.workspace_size(w.B, w.Hq, w.Hkv, w.D, w.qLen, w.kv_cap, w.causal, dt,
+                                 args.num_splits)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(g.q)
+    out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.qLen), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def call():
-        mx.fwd_kvcache(g.q, g.k_cache, g.v_cache, g.cache_seqlens, w.causal, out=out,
-                       lse=lse, num_splits=args.num_splits, workspace=ws,
-                       stream=stream.cuda_stream)
+        if P:
+            mx.fwd_kvcache_paged(q, paged.k_pages, paged.v_pages, paged.block_table,
+                                 paged.cache_seqlens, w.causal, out=out, lse=lse,
+                                 num_splits=args.num_splits, workspace=ws,
+                                 stream=stream.cuda_stream)
+        else:
+            mx.fwd_kvcache(q, g.k_cache, g.v_cache, g.cache_seqlens, w.causal, out=out,
+                           lse=lse, num_splits=args.num_splits, workspace=ws,
+                           stream=stream.cuda_stream)
 
     for _ in range(args.warmup):
         call()
@@ -243,18 +261,26 @@ def main():
     alg_bytes = wl.algorithmic_bytes(w, lens)
     kv = wl.kv_bytes(w, lens)
     q_bytes = w.B * w.qLen * w.Hq * w.D * w.elt
-    split_bytes = kv + q_bytes
+    # a paged cache also reads one block-table entry per page touched
+    bt_bytes = sum(-(-max(0, min(n, w.kv_cap)) // P) for n in lens) * 4 if P else 0
+    alg_bytes += bt_bytes
+    split_bytes = kv + q_bytes + bt_bytes
     gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
     split_gbs = split_bytes / (split_ms_mean * 1e-3) / 1e9
-    traffic = traffic_for(w.name)
+    traffic = traffic_for(f"{w.name}_paged{P}" if P else w.name)
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         threads = args.cpu_threads or len(os.sched_getaffinity(0))
         tc = time.perf_counter()
-        oracle.attention(inp.q, inp.k_cache, inp.v_cache, inp.cache_seqlens, w.causal,
-                         w.dtype, nthreads=threads)
+        if P:
+            oracle.attention_paged(inp.q, paged_cpu.k_pages, paged_cpu.v_pages,
+                                   paged_cpu.block_table, paged_cpu.cache_seqlens, w.causal,
+                                   w.dtype, nthreads=threads)
+        else:
+            oracle.attention(inp.q, inp.k_cache, inp.v_cache, inp.cache_seqlens, w.causal,
+                             w.dtype, nthreads=threads)
         cpu_s = time.perf_counter() - tc
         cpu = {"value": round(alg_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
@@ -276,7 +302,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "qLen": w.qLen, "Hq": w.Hq, "Hkv": w.Hkv,
                    "D": w.D, "kv_cap": w.kv_cap, "sum_kv_len": int(sum(lens)),
-                   "causal": w.causal, "parallelism": "single GPU"},
+                   "causal": w.causal, "kv_layout": f"paged{P}" if P else "contiguous",
+                   "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "attn_calls_per_s": round(1e3 / ms_per_step, 1),
         "plan": plan,

@@ -84,7 +84,7 @@ typedef enum { MXFA_FP16 = 0, MXFA_BF16 = 1 } mxfa_dtype;
 
 typedef enum {
     MXFA_PATH_VALU = 0,         /* vector-ALU split kernel (few rows per kv head) */
-    MXFA_PATH_MFMA = 1          /* matrix-core split kernel (>= 8 rows per kv head) */
+    MXFA_PATH_MFMA = 1          /* matrix-core split kernel (>= 32 rows per kv head) */
 } mxfa_path;
 
 /* How a call is carried out.  The analogue of the dispatch record the
@@ -152,6 +152,55 @@ MXFA_API mxfa_status mxfa_workspace_size(int B, int Hq, int Hkv, int D,
                                          int qLen, int kv_cap, int causal,
                                          int dtype, int num_splits,
                                          size_t *bytes);
+
+/* Paged KV cache.  The MXFlashAttn sdist README lists a paged KV cache among
+ * its implemented layouts (capability matrix) and describes its kernel as a
+ * split-KV paged decode kernel (introduction); the pages give no layout, so
+ * the FlashAttention-style block table is taken:
+ *     k_pages,
+ *     v_pages      [num_pages, page_size, Hkv, D]   a pool of fixed-size pages
+ *     block_table  int32 [B, max_pages]             page of each block of
+ *                                                   page_size tokens
+ * Token j of sequence b is row j % page_size of page
+ * block_table[b * max_pages + j / page_size]; every other convention is the
+ * contiguous cache's with kv_cap = max_pages * page_size (cache_seqlens are
+ * clamped to it; NULL means every sequence holds max_pages * page_size
+ * tokens).  Only the entries for blocks below n_b are read; they should lie
+ * in [0, num_pages), and a value outside is clamped into it (never an
+ * out-of-pool access).  Pages may be shared between sequences and appear in
+ * any order.  page_size must be a power of two >= 16 (else
+ * MXFA_ERR_UNSUPPORTED; page_size <= 0 is MXFA_ERR_INVALID_ARG) and one
+ * page must stay below 2^30 bytes; max_pages * page_size must fit an int.
+ * block_table must be non-NULL and 4-byte aligned when max_pages > 0, and
+ * num_pages >= 1 then.  The plan, scratch and merge are those of the
+ * contiguous cache with the same kv_cap. */
+MXFA_API mxfa_status mxfa_fwd_kvcache_paged(const void *q, const void *k_pages,
+                                            const void *v_pages,
+                                            const int32_t *block_table,
+                                            const int32_t *cache_seqlens,
+                                            void *out, float *lse, int B, int Hq,
+                                            int Hkv, int D, int qLen,
+                                            int num_pages, int page_size,
+                                            int max_pages, int causal, int dtype,
+                                            void *stream);
+
+/* Paged cache with caller-provided scratch and an optional forced partition
+ * count; num_splits and workspace as for mxfa_fwd_kvcache_ws, the size from
+ * mxfa_workspace_size_paged. */
+MXFA_API mxfa_status mxfa_fwd_kvcache_paged_ws(
+    const void *q, const void *k_pages, const void *v_pages,
+    const int32_t *block_table, const int32_t *cache_seqlens, void *out,
+    float *lse, int B, int Hq, int Hkv, int D, int qLen, int num_pages,
+    int page_size, int max_pages, int causal, int dtype, int num_splits,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes that mxfa_fwd_kvcache_paged_ws needs (the pool size does not
+ * enter); same validation and device rules as mxfa_workspace_size. */
+MXFA_API mxfa_status mxfa_workspace_size_paged(int B, int Hq, int Hkv, int D,
+                                               int qLen, int page_size,
+                                               int max_pages, int causal,
+                                               int dtype, int num_splits,
+                                               size_t *bytes);
 
 /* The plan (path, partitioning, grid, scratch size) for a problem on a
  * device with num_cus compute units (num_cus <= 0 means 256, an MI355X).

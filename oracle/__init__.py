@@ -166,6 +166,50 @@ def attention_rows(q, k_cache, v_cache, rows: Sequence[Tuple[int, int, int]],
     return out, lse
 
 
+def gather_pages(k_pages, v_pages, block_table, cache_seqlens=None):
+    """The contiguous cache a paged cache stands for.
+
+    A paged KV cache is among the layouts the MXFlashAttn sdist README lists
+    (capability matrix); the pages give no layout, and the FlashAttention
+    block-table convention is read: token j of sequence b is row j % P of
+    page block_table[b, j // P], P the page size.  Returns (k, v) bit patterns
+    [B, max_pages * P, Hkv, D] and the lengths; rows at or past a sequence's
+    length are zero and are never read.  Every block-table entry that is read
+    must name a page of the pool."""
+    kp, vp = _as_u16(k_pages), _as_u16(v_pages)
+    num_pages, P, Hkv, D = kp.shape
+    assert vp.shape == kp.shape
+    try:
+        import torch
+        if isinstance(block_table, torch.Tensor):
+            block_table = block_table.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    bt = np.asarray(block_table, dtype=np.int64)
+    B, max_pages = bt.shape
+    cap = max_pages * P
+    sl = _seqlens(cache_seqlens, B)
+    lens = [cap] * B if sl is None else [max(0, min(int(x), cap)) for x in sl]
+    k = np.zeros((B, cap, Hkv, D), dtype=np.uint16)
+    v = np.zeros((B, cap, Hkv, D), dtype=np.uint16)
+    for b, n in enumerate(lens):
+        j = np.arange(n)
+        pages = bt[b, j // P]
+        if n and (pages.min() < 0 or pages.max() >= num_pages):
+            raise ValueError(f"block table of sequence {b} names a page outside the pool")
+        k[b, :n] = kp[pages, j % P]
+        v[b, :n] = vp[pages, j % P]
+    return k, v, np.asarray(lens, dtype=np.int32)
+
+
+def attention_paged(q, k_pages, v_pages, block_table, cache_seqlens=None,
+                    causal: bool = False, dtype: Optional[str] = None, nthreads: int = 0,
+                    lib_path: str = LIB_PATH) -> Tuple[np.ndarray, np.ndarray]:
+    """``attention`` over the contiguous cache ``gather_pages`` forms."""
+    k, v, lens = gather_pages(k_pages, v_pages, block_table, cache_seqlens)
+    return attention(q, k, v, lens, causal, dtype, nthreads, lib_path)
+
+
 def decode16(bits: np.ndarray, dtype: str, lib_path: str = LIB_PATH) -> np.ndarray:
     """Decode an array of 16-bit patterns to float64 with the oracle's decoder."""
     lib = load(lib_path)

@@ -19,9 +19,11 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxGridYZ = 65535;
 constexpr size_t kWsAlign = 256;
 
-// Problem-size checks only; pointers are checked separately.
+// Problem-size checks only; pointers are checked separately.  A paged
+// cache has page_size > 0 and kv_cap = max_pages * page_size.
 struct Problem {
     int B, Hq, Hkv, D, qLen, kv_cap, causal, dtype;
+    int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
 thread_local mxfa_plan_t t_last_plan;
@@ -51,12 +53,42 @@ mxfa_status check_problem(const Problem &p) {
         return MXFA_ERR_INVALID_ARG;
     if (p.D != 64 && p.D != 128) return MXFA_ERR_UNSUPPORTED;
     if (p.B > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
+    if (p.page_size > 0) {
+        // paged: the pool's byte size must be representable; one page is
+        // addressed with 32-bit offsets, so it must stay below 2^30 bytes
+        if (!mul_ok((uint64_t)p.num_pages, (uint64_t)p.page_size, &x) ||
+            !mul_ok(x, (uint64_t)p.Hkv, &x) || !mul_ok(x, (uint64_t)p.D, &x) ||
+            !mul_ok(x, 2, &x) || x > (UINT64_C(1) << 62))
+            return MXFA_ERR_INVALID_ARG;
+        if ((uint64_t)p.page_size * p.Hkv * p.D * 2 > (UINT64_C(1) << 30))
+            return MXFA_ERR_UNSUPPORTED;
+        return MXFA_OK;
+    }
     // K/V are addressed with 32-bit byte offsets inside one sequence; loads
     // issued ahead may run up to 1024 tokens past the cache, so both the
     // cache and that slack must stay below 2^30 bytes
     if ((uint64_t)p.kv_cap * p.Hkv * p.D * 2 > (UINT64_C(1) << 30)) return MXFA_ERR_UNSUPPORTED;
     if ((uint64_t)1024 * p.Hkv * p.D * 2 > (UINT64_C(1) << 30)) return MXFA_ERR_UNSUPPORTED;
     return MXFA_OK;
+}
+
+// A paged problem: page_size a power of two >= kMinPage (a smaller or
+// irregular page is a valid layout the kernels do not implement), the
+// logical capacity max_pages * page_size an int, and at least one page when
+// sequences may hold tokens.
+mxfa_status paged_problem(int B, int Hq, int Hkv, int D, int qLen, int num_pages,
+                          int page_size, int max_pages, int causal, int dtype, Problem *out) {
+    if (num_pages < 0 || page_size <= 0 || max_pages < 0) return MXFA_ERR_INVALID_ARG;
+    if (max_pages > 0 && num_pages == 0) return MXFA_ERR_INVALID_ARG;
+    if ((page_size & (page_size - 1)) != 0 || page_size < kMinPage) return MXFA_ERR_UNSUPPORTED;
+    if ((int64_t)max_pages * page_size > INT32_MAX) return MXFA_ERR_UNSUPPORTED;
+    Problem p{B, Hq, Hkv, D, qLen, max_pages * page_size, causal, dtype};
+    p.page_size = page_size;
+    p.max_pages = max_pages;
+    p.num_pages = num_pages;
+    const mxfa_status st = check_problem(p);
+    if (st == MXFA_OK) *out = p;
+    return st;
 }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -230,8 +262,8 @@ mxfa_status device_cus(int *cus) {
 }
 
 mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seqlens,
-                void *out, float *lse, const Problem &p, const FullPlan &f, void *ws,
-                hipStream_t stream) {
+                const int32_t *block_table, void *out, float *lse, const Problem &p,
+                const FullPlan &f, void *ws, hipStream_t stream) {
     const mxfa_plan_t &pl = f.pub;
     KernelArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -239,6 +271,12 @@ mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seql
     a.k = k;
     a.v = v;
     a.seqlens = seqlens;
+    if (p.page_size > 0) {
+        a.block_table = block_table;
+        a.max_pages = p.max_pages;
+        a.num_pages = p.num_pages;
+        a.log_page = __builtin_ctz((unsigned)p.page_size);
+    }
     a.out = out;
     a.lse = lse;
     if (pl.combine) {
@@ -278,6 +316,33 @@ mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seql
 void record(const mxfa_plan_t &pl) {
     t_last_plan = pl;
     t_has_last = true;
+}
+
+// Plan and launch a checked problem.  own_ws: allocate the scratch on the
+// stream (stream-ordered) instead of using the caller's.
+mxfa_status execute(const void *q, const void *k, const void *v, const int32_t *seqlens,
+                    const int32_t *block_table, void *out, float *lse, const Problem &p,
+                    int num_splits, void *workspace, size_t workspace_bytes, bool own_ws,
+                    hipStream_t s) {
+    if (!own_ws && workspace && !aligned(workspace, kWsAlign)) return MXFA_ERR_INVALID_ARG;
+    int cus = 0;
+    mxfa_status st = device_cus(&cus);
+    if (st != MXFA_OK) return st;
+    FullPlan f;
+    st = make_plan(p, num_splits, cus, &f);
+    if (st != MXFA_OK) return st;
+    void *ws = workspace;
+    if (own_ws) {
+        ws = nullptr;
+        if (f.pub.workspace_bytes > 0 && hipMallocAsync(&ws, f.pub.workspace_bytes, s) != hipSuccess)
+            return MXFA_ERR_HIP;
+    } else if (f.pub.workspace_bytes > 0 && (!workspace || workspace_bytes < f.pub.workspace_bytes)) {
+        return MXFA_ERR_WORKSPACE;
+    }
+    st = run(q, k, v, seqlens, block_table, out, lse, p, f, ws, s);
+    if (own_ws && ws && hipFreeAsync(ws, s) != hipSuccess && st == MXFA_OK) st = MXFA_ERR_HIP;
+    if (st == MXFA_OK) record(f.pub);
+    return st;
 }
 
 }  // namespace
@@ -326,18 +391,8 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_ws(const void *q, const void *k_cache, con
     if (B == 0 || qLen == 0) return MXFA_OK;       // nothing to compute
     st = check_pointers(q, k_cache, v_cache, cache_seqlens, out, lse, kv_cap);
     if (st != MXFA_OK) return st;
-    if (workspace && !aligned(workspace, kWsAlign)) return MXFA_ERR_INVALID_ARG;
-    int cus = 0;
-    st = device_cus(&cus);
-    if (st != MXFA_OK) return st;
-    FullPlan f;
-    st = make_plan(p, num_splits, cus, &f);
-    if (st != MXFA_OK) return st;
-    if (f.pub.workspace_bytes > 0 && (!workspace || workspace_bytes < f.pub.workspace_bytes))
-        return MXFA_ERR_WORKSPACE;
-    st = run(q, k_cache, v_cache, cache_seqlens, out, lse, p, f, workspace, (hipStream_t)stream);
-    if (st == MXFA_OK) record(f.pub);
-    return st;
+    return execute(q, k_cache, v_cache, cache_seqlens, nullptr, out, lse, p, num_splits,
+                   workspace, workspace_bytes, false, (hipStream_t)stream);
 }
 
 MXFA_API mxfa_status mxfa_fwd_kvcache(const void *q, const void *k_cache, const void *v_cache,
@@ -350,20 +405,62 @@ MXFA_API mxfa_status mxfa_fwd_kvcache(const void *q, const void *k_cache, const 
     if (B == 0 || qLen == 0) return MXFA_OK;
     st = check_pointers(q, k_cache, v_cache, cache_seqlens, out, lse, kv_cap);
     if (st != MXFA_OK) return st;
+    return execute(q, k_cache, v_cache, cache_seqlens, nullptr, out, lse, p, 0, nullptr, 0,
+                   true, (hipStream_t)stream);
+}
+
+MXFA_API mxfa_status mxfa_workspace_size_paged(int B, int Hq, int Hkv, int D, int qLen,
+                                               int page_size, int max_pages, int causal,
+                                               int dtype, int num_splits, size_t *bytes) {
+    if (!bytes || num_splits < 0) return MXFA_ERR_INVALID_ARG;
+    Problem p;
+    // the plan does not depend on the pool size: any positive page count
+    mxfa_status st = paged_problem(B, Hq, Hkv, D, qLen, 1, page_size, max_pages, causal,
+                                   dtype, &p);
+    if (st != MXFA_OK) return st;
     int cus = 0;
     st = device_cus(&cus);
     if (st != MXFA_OK) return st;
     FullPlan f;
-    st = make_plan(p, 0, cus, &f);
+    st = make_plan(p, num_splits, cus, &f);
     if (st != MXFA_OK) return st;
-    hipStream_t s = (hipStream_t)stream;
-    void *ws = nullptr;
-    if (f.pub.workspace_bytes > 0 && hipMallocAsync(&ws, f.pub.workspace_bytes, s) != hipSuccess)
-        return MXFA_ERR_HIP;
-    st = run(q, k_cache, v_cache, cache_seqlens, out, lse, p, f, ws, s);
-    if (ws && hipFreeAsync(ws, s) != hipSuccess && st == MXFA_OK) st = MXFA_ERR_HIP;
-    if (st == MXFA_OK) record(f.pub);
-    return st;
+    *bytes = (B == 0 || qLen == 0) ? 0 : f.pub.workspace_bytes;
+    return MXFA_OK;
+}
+
+MXFA_API mxfa_status mxfa_fwd_kvcache_paged_ws(
+    const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+    const int32_t *cache_seqlens, void *out, float *lse, int B, int Hq, int Hkv, int D,
+    int qLen, int num_pages, int page_size, int max_pages, int causal, int dtype,
+    int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p;
+    mxfa_status st = paged_problem(B, Hq, Hkv, D, qLen, num_pages, page_size, max_pages,
+                                   causal, dtype, &p);
+    if (st != MXFA_OK) return st;
+    if (num_splits < 0) return MXFA_ERR_INVALID_ARG;
+    if (B == 0 || qLen == 0) return MXFA_OK;
+    st = check_pointers(q, k_pages, v_pages, cache_seqlens, out, lse, p.kv_cap);
+    if (st != MXFA_OK) return st;
+    if (p.kv_cap > 0 && (!block_table || !aligned(block_table, 4))) return MXFA_ERR_INVALID_ARG;
+    return execute(q, k_pages, v_pages, cache_seqlens, block_table, out, lse, p, num_splits,
+                   workspace, workspace_bytes, false, (hipStream_t)stream);
+}
+
+MXFA_API mxfa_status mxfa_fwd_kvcache_paged(
+    const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+    const int32_t *cache_seqlens, void *out, float *lse, int B, int Hq, int Hkv, int D,
+    int qLen, int num_pages, int page_size, int max_pages, int causal, int dtype,
+    void *stream) {
+    Problem p;
+    mxfa_status st = paged_problem(B, Hq, Hkv, D, qLen, num_pages, page_size, max_pages,
+                                   causal, dtype, &p);
+    if (st != MXFA_OK) return st;
+    if (B == 0 || qLen == 0) return MXFA_OK;
+    st = check_pointers(q, k_pages, v_pages, cache_seqlens, out, lse, p.kv_cap);
+    if (st != MXFA_OK) return st;
+    if (p.kv_cap > 0 && (!block_table || !aligned(block_table, 4))) return MXFA_ERR_INVALID_ARG;
+    return execute(q, k_pages, v_pages, cache_seqlens, block_table, out, lse, p, 0, nullptr, 0,
+                   true, (hipStream_t)stream);
 }
 
 MXFA_API mxfa_status mxfa_last_plan(mxfa_plan_t *plan) {

@@ -32,9 +32,15 @@ enum Schedule { kFixed = 0, kBalanced = 1 };
 // A workgroup that covers a whole stream writes the final output instead.
 struct KernelArgs {
     const void *q;            // [B, qLen, Hq, D]
-    const void *k;            // [B, kv_cap, Hkv, D]
-    const void *v;            // [B, kv_cap, Hkv, D]
+    const void *k;            // [B, kv_cap, Hkv, D], or pages [num_pages, page, Hkv, D]
+    const void *v;            // same layout as k
     const int32_t *seqlens;   // [B] or nullptr
+    // Paged cache: token j of sequence b is row j % page of page
+    // block_table[b * max_pages + j / page]; nullptr for a contiguous cache.
+    // kv_cap is then max_pages * page.
+    const int32_t *block_table;
+    int max_pages, num_pages;
+    int log_page;             // log2(page), page a power of two >= kMinPage
     void *out;                // [B, qLen, Hq, D]
     float *lse;               // [B, Hq, qLen] or nullptr
     float *ws_o;              // [slots][head_block][row_block][D]
@@ -53,6 +59,11 @@ struct KernelArgs {
     int min_share;            // kBalanced: lower bound on tokens per workgroup
     float qscale;             // log2(e) / sqrt(D)
 };
+
+// Smallest page of a paged cache: a load step of the VALU kernel (at most 16
+// tokens) and a load of the matrix-core kernel (4 or 8 consecutive tokens)
+// then never span two pages.
+constexpr int kMinPage = 16;
 
 // Largest batch the balanced schedule handles (its length prefix sums are
 // kept in LDS by every workgroup).

@@ -34,6 +34,14 @@
 //   channel p of the 4 keys).  One V^T operand serves all 4 row tiles.
 // V rows are stored in LDS with their 16-byte chunks XOR-swizzled by the key
 // index, so the keys read by one transposed read hit distinct banks.
+//
+// Paged caches.  With a block table, token j of sequence b is row j % page of
+// page block_table[b][j / page].  Tiles are then aligned to multiples of 32
+// tokens and each 16-byte load instruction covers 4 (D = 128) or 8 (D = 64)
+// consecutive tokens, all in one page since page >= 16: the page is looked up
+// per load (a scalar load) and read through a descriptor whose range ends at
+// the page's last valid token.  Keys of the first tile that precede the
+// segment are masked.
 #include "device_common.h"
 #include "launch.h"
 #include "schedule.h"
@@ -86,7 +94,7 @@ __device__ __forceinline__ float group_sum(float x) {
     return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-template <int DT, int D>
+template <int DT, int D, bool PAGED>
 struct Mfma {
     using T = MfmaType<DT>;
     typedef typename T::vec vec;
@@ -145,7 +153,9 @@ struct Mfma {
             t_end = max(t_end, t_lo);   // an empty segment, never a negative range
         }
         t_end = __builtin_amdgcn_readfirstlane(t_end);
-        const int ntiles = t_end > t_lo ? (t_end - t_lo + kKT - 1) / kKT : 0;
+        // first key of tile 0: a paged cache is read in page-aligned tiles
+        const int t_base = PAGED ? (t_lo & ~(kKT - 1)) : t_lo;
+        const int ntiles = t_end > t_lo ? (t_end - t_base + kKT - 1) / kKT : 0;
         const int my_tiles = ntiles > wave ? (ntiles - wave + kMWaves - 1) / kMWaves : 0;
 
         // the lane's query row p of each row tile, as the B operand of S^T =
@@ -174,8 +184,10 @@ struct Mfma {
         const uint32_t tok_bytes = (uint32_t)a.Hkv * D * 2;
         const size_t seq_off = (size_t)b * a.kv_cap * a.Hkv * D;
         const uint32_t range = (uint32_t)t_end * tok_bytes;
-        const __amdgpu_buffer_rsrc_t krsrc = make_rsrc((const uint16_t *)a.k + seq_off, range);
-        const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc((const uint16_t *)a.v + seq_off, range);
+        const __amdgpu_buffer_rsrc_t krsrc =
+            make_rsrc((const uint16_t *)a.k + (PAGED ? 0 : seq_off), range);
+        const __amdgpu_buffer_rsrc_t vrsrc =
+            make_rsrc((const uint16_t *)a.v + (PAGED ? 0 : seq_off), range);
         // K and V row-major: lane l loads chunk l % NCH of key l / NCH (+ VKEYS u)
         const int vch = lane % NCH;
         const int vkey = lane / NCH;
@@ -185,17 +197,59 @@ struct Mfma {
         // tile index of the wave's i-th tile; indices past the segment are
         // clamped to ntiles, whose keys all lie past t_end (loads read nothing)
         auto tile_of = [&](int i) { return min(wave + kMWaves * i, ntiles); };
-        auto gload_v = [&](int j) {
-            const uint32_t base = (uint32_t)(t_lo + j * kKT) * tok_bytes;
+        // paged: a tile (32 keys, aligned) lies in one page, or in two when the
+        // page is 16 tokens; its block-table entries are read with vector
+        // loads one tile ahead (tracked with the K/V loads, no scalar-cache
+        // wait in the loop) through a descriptor that ends at the last page
+        // holding a token below t_end (entries past it read as 0 and are not
+        // used).  pg_cur: the pages of the tile loaded next.
+        const int page = 1 << a.log_page;
+        const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(
+            PAGED ? (const void *)(a.block_table + (size_t)b * a.max_pages) : nullptr,
+            PAGED ? (uint32_t)((t_end + page - 1) >> a.log_page) * 4u : 0u);
+        uint32_t pg_cur[2] = {0u, 0u};
+        auto fetch_pages = [&](int j, uint32_t (&pg)[2]) {
+            const int t0 = t_base + j * kKT;
 #pragma unroll
-            for (int u = 0; u < LDV; ++u)
-                vs[u] = load16(vrsrc, base + vofs + (uint32_t)(u * VKEYS) * tok_bytes);
+            for (int h = 0; h < 2; ++h)
+                pg[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                    bt_rsrc, (uint32_t)((t0 + 16 * h) >> a.log_page) * 4u, 0, 0);
+        };
+        // the load of tokens tok .. tok + VKEYS - 1 (tok a multiple of VKEYS,
+        // in half h of its tile) from page entry e, through a descriptor whose
+        // range ends at the last token below t_end
+        auto page_load = [&](const void *pool, int tok, uint32_t e) {
+            const int pi = tok >> a.log_page;
+            const int valid = t_end - (pi << a.log_page);
+            const int pg = clampi(__builtin_amdgcn_readfirstlane((int)e), 0, a.num_pages - 1);
+            const uint32_t rng = valid <= 0 ? 0u : (uint32_t)min(valid, page) * tok_bytes;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(
+                (const uint16_t *)pool + ((size_t)pg << a.log_page) * a.Hkv * D, rng);
+            return load16(r, (uint32_t)(tok & (page - 1)) * tok_bytes + vofs);
+        };
+        auto gload_v = [&](int j) {
+            if constexpr (PAGED) {
+#pragma unroll
+                for (int u = 0; u < LDV; ++u)
+                    vs[u] = page_load(a.v, t_base + j * kKT + u * VKEYS, pg_cur[u * VKEYS >= 16]);
+            } else {
+                const uint32_t base = (uint32_t)(t_lo + j * kKT) * tok_bytes;
+#pragma unroll
+                for (int u = 0; u < LDV; ++u)
+                    vs[u] = load16(vrsrc, base + vofs + (uint32_t)(u * VKEYS) * tok_bytes);
+            }
         };
         auto gload_k = [&](int j) {
-            const uint32_t base = (uint32_t)(t_lo + j * kKT) * tok_bytes;
+            if constexpr (PAGED) {
 #pragma unroll
-            for (int u = 0; u < LDK; ++u)
-                ks[u] = load16(krsrc, base + vofs + (uint32_t)(u * VKEYS) * tok_bytes);
+                for (int u = 0; u < LDK; ++u)
+                    ks[u] = page_load(a.k, t_base + j * kKT + u * VKEYS, pg_cur[u * VKEYS >= 16]);
+            } else {
+                const uint32_t base = (uint32_t)(t_lo + j * kKT) * tok_bytes;
+#pragma unroll
+                for (int u = 0; u < LDK; ++u)
+                    ks[u] = load16(krsrc, base + vofs + (uint32_t)(u * VKEYS) * tok_bytes);
+            }
         };
 
         // online softmax with a lazily moved reference: every lane keeps the
@@ -212,17 +266,25 @@ struct Mfma {
             for (int db = 0; db < DB; ++db) o[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        auto compute = [&](int set, int j, int jn) {
-            const int key0 = t_lo + j * kKT;
+        auto compute = [&](int set, int j, int jn, int jnn) {
+            const int key0 = t_base + j * kKT;
+            // paged: keys of the first tile before t_lo are not part of the segment
+            const int vis_lo = (PAGED && key0 < t_lo) ? t_lo - key0 - 4 * g : INT32_MIN;
             // stage this tile's K and V rows in the wave's LDS buffer `set`
 #pragma unroll
             for (int u = 0; u < LDK; ++u)
                 *(u32x4 *)(sm.buf + t_off(wave, set, 0, vkey + u * VKEYS, vch)) = ks[u];
             gload_k(jn);       // the next tile streams while this one is computed
+            uint32_t pg_nxt[2];
+            if constexpr (PAGED) fetch_pages(jnn, pg_nxt);
 #pragma unroll
             for (int u = 0; u < LDV; ++u)
                 *(u32x4 *)(sm.buf + t_off(wave, set, 1, vkey + u * VKEYS, vch)) = vs[u];
             gload_v(jn);
+            if constexpr (PAGED) {
+                pg_cur[0] = pg_nxt[0];
+                pg_cur[1] = pg_nxt[1];
+            }
             wave_lds_sync();   // the tiles written above are visible to the whole wave
             // S^T for 4 row tiles x 2 blocks of 16 keys, in log2 units; the A
             // operand (16 keys x 32 channels of K) serves all row tiles
@@ -248,7 +310,8 @@ struct Mfma {
                         acc = T::mma(ka[kb][kk], qf[rt][kk], acc);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float v = 16 * kb + i <= vis ? acc[i] * a.qscale : kNegInf;
+                        const float v = (16 * kb + i <= vis && 16 * kb + i >= vis_lo)
+                                            ? acc[i] * a.qscale : kNegInf;
                         x[rt][kb][i] = v;
                         mloc[rt] = fmaxf(mloc[rt], v);
                     }
@@ -302,11 +365,13 @@ struct Mfma {
         };
         // one tile in flight per wave: the next tile's loads are issued as
         // soon as this tile is in LDS
+        if constexpr (PAGED) fetch_pages(tile_of(0), pg_cur);
         gload_v(tile_of(0));
         gload_k(tile_of(0));
+        if constexpr (PAGED) fetch_pages(tile_of(1), pg_cur);
         for (int i = 0; i < my_tiles; ++i) {
             const int j = tile_of(i);
-            compute(i & 1, j, tile_of(i + 1));
+            compute(i & 1, j, tile_of(i + 1), tile_of(i + 2));
         }
 
         // the row sums over the 4 lanes of each row
@@ -379,11 +444,11 @@ struct Mfma {
 // One workgroup per CU, one wave per SIMD: each wave keeps 64 rows of
 // accumulators and two K/V tiles in registers.
 
-template <int DT, int D, int SCHED>
+template <int DT, int D, int SCHED, bool PAGED>
 __global__ __launch_bounds__(kMWaves * 64)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_kv_mfma_kernel(KernelArgs a) {
-    using M = Mfma<DT, D>;
+    using M = Mfma<DT, D, PAGED>;
     __shared__ __attribute__((aligned(16))) typename M::Smem sm;
     drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
                                  bool whole) {
@@ -395,9 +460,13 @@ template <int DT, int D>
 hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
     KernelArgs args = a;
     void *kargs[] = {&args};
-    const void *fn = a.schedule == kBalanced
-        ? (const void *)&split_kv_mfma_kernel<DT, D, kBalanced>
-        : (const void *)&split_kv_mfma_kernel<DT, D, kFixed>;
+    const bool paged = a.block_table != nullptr;
+    const void *fn =
+        a.schedule == kBalanced
+            ? (paged ? (const void *)&split_kv_mfma_kernel<DT, D, kBalanced, true>
+                     : (const void *)&split_kv_mfma_kernel<DT, D, kBalanced, false>)
+            : (paged ? (const void *)&split_kv_mfma_kernel<DT, D, kFixed, true>
+                     : (const void *)&split_kv_mfma_kernel<DT, D, kFixed, false>);
     return hipLaunchKernel(fn, grid, dim3(kMWaves * 64), kargs, 0, stream);
 }
 

@@ -58,6 +58,13 @@
 // one or more stream segments that fall into it; this keeps all workgroups
 // equally loaded however ragged the sequence lengths are.  The lengths are
 // read on the device, so each workgroup first forms their prefix sums.
+//
+// Paged caches.  With a block table, token j of sequence b is row j % page of
+// page block_table[b][j / page].  Steps are then aligned to multiples of
+// TSTEP tokens (at most 16, and page >= 16), so the tokens of one step lie in
+// one page: the page is looked up once per step (a scalar load) and the step
+// reads through a buffer descriptor whose range ends at the page's last valid
+// token.  Tokens of the first step that precede the segment are masked.
 #include "device_common.h"
 #include "launch.h"
 #include "schedule.h"
@@ -112,7 +119,7 @@ struct Halve {
     }
 };
 
-template <int DT, int D, int RB, int HS, int HG>
+template <int DT, int D, int RB, int HS, int HG, bool PAGED>
 struct Valu {
     static constexpr int LPT = D / 8;                  // lanes per slot
     static constexpr int LB = ilog2(LPT);              // 4 (D=128) or 3 (D=64)
@@ -120,7 +127,9 @@ struct Valu {
     static constexpr int TSUB = TPW / HS;              // token sub-slots per wave
     static constexpr int TI = kWaves / HG;             // token interleave across waves
     static constexpr int HPW = HG * HS;                // kv heads per workgroup
-    static constexpr int U = (LPT / RB) >= 4 ? 4 : (LPT / RB);  // tokens per slot per step
+    static constexpr int U0 = (LPT / RB) >= 4 ? 4 : (LPT / RB);
+    // tokens per slot per step; a paged step stays within kMinPage tokens
+    static constexpr int U = (PAGED && U0 * TSUB > kMinPage) ? kMinPage / TSUB : U0;
     static constexpr int N = U * RB;                   // partial scores per lane per step
     static constexpr int H = ilog2(N);                 // halving steps
     static constexpr int LOGRB = ilog2(RB);
@@ -171,7 +180,9 @@ struct Valu {
             t_hi = min(t_hi, i_max + n - a.qLen + 1);
             t_hi = max(t_hi, t_lo);     // an empty segment, never a negative range
         }
-        const int nsteps = t_hi > t_lo ? (t_hi - t_lo + TSTEP - 1) / TSTEP : 0;
+        // first token of step 0: a paged cache is read in page-aligned steps
+        const int t_base = PAGED ? (t_lo & ~(TSTEP - 1)) : t_lo;
+        const int nsteps = t_hi > t_lo ? (t_hi - t_base + TSTEP - 1) / TSTEP : 0;
 
         // lane permutation of the reduce-scatter
         const int gperm = sl ^ (((sl >> 2) & 1) * 3);
@@ -208,8 +219,10 @@ struct Valu {
         const uint32_t tok_bytes = (uint32_t)a.Hkv * D * 2;
         const size_t seq_off = (size_t)b * a.kv_cap * a.Hkv * D;
         const uint32_t range = (uint32_t)t_hi * tok_bytes;
-        const __amdgpu_buffer_rsrc_t krsrc = make_rsrc((const uint16_t *)a.k + seq_off, range);
-        const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc((const uint16_t *)a.v + seq_off, range);
+        const __amdgpu_buffer_rsrc_t krsrc =
+            make_rsrc((const uint16_t *)a.k + (PAGED ? 0 : seq_off), range);
+        const __amdgpu_buffer_rsrc_t vrsrc =
+            make_rsrc((const uint16_t *)a.v + (PAGED ? 0 : seq_off), range);
         const uint32_t lane_base = head_ok ? (uint32_t)kvh * D * 2 + 16u * sl : 0x80000000u;
         uint32_t koff[U], voff[U];
 #pragma unroll
@@ -226,11 +239,34 @@ struct Valu {
             for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
 
         auto load_step = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[U]) {
-            const uint32_t base = (uint32_t)(t_lo + st * TSTEP) * tok_bytes;
+            if constexpr (PAGED) {
+                // the step's page; its descriptors end at the last token
+                // below t_hi (no range when the step lies past it)
+                const int tb = t_base + st * TSTEP;
+                const int pi = tb >> a.log_page;
+                const int valid = t_hi - (pi << a.log_page);
+                const int page = 1 << a.log_page;
+                int pg = 0;
+                if (valid > 0)
+                    pg = clampi(a.block_table[(size_t)b * a.max_pages + pi], 0, a.num_pages - 1);
+                pg = __builtin_amdgcn_readfirstlane(pg);
+                const uint32_t rng = valid <= 0 ? 0u : (uint32_t)min(valid, page) * tok_bytes;
+                const size_t poff = ((size_t)pg << a.log_page) * a.Hkv * D;
+                const __amdgpu_buffer_rsrc_t kp = make_rsrc((const uint16_t *)a.k + poff, rng);
+                const __amdgpu_buffer_rsrc_t vp = make_rsrc((const uint16_t *)a.v + poff, rng);
+                const uint32_t base = (uint32_t)(tb & (page - 1)) * tok_bytes;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                kr[u] = load16(krsrc, base + koff[u]);
-                vr[u] = load16(vrsrc, base + voff[u]);
+                for (int u = 0; u < U; ++u) {
+                    kr[u] = load16(kp, base + koff[u]);
+                    vr[u] = load16(vp, base + voff[u]);
+                }
+            } else {
+                const uint32_t base = (uint32_t)(t_lo + st * TSTEP) * tok_bytes;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    kr[u] = load16(krsrc, base + koff[u]);
+                    vr[u] = load16(vrsrc, base + voff[u]);
+                }
             }
         };
 
@@ -250,8 +286,8 @@ struct Valu {
             Halve<LB, N, 0, H>::run(v);
             const float s = AllReduce<LB, H, LB>::sum(v[0]);
 
-            const int tok = t_lo + st * TSTEP + phiu * TSUB + ts;
-            const bool vis = row_ok && tok < t_hi && tok <= causal_last;
+            const int tok = t_base + st * TSTEP + phiu * TSUB + ts;
+            const bool vis = row_ok && tok < t_hi && tok <= causal_last && (!PAGED || tok >= t_lo);
             const float x = vis ? s * a.qscale : kNegInf;
 
             const float mx = AllReduce<LB, 0, LOGU>::max(x);
@@ -376,11 +412,11 @@ struct Valu {
     }
 };
 
-template <int DT, int D, int RB, int HS, int HG, int SCHED>
+template <int DT, int D, int RB, int HS, int HG, int SCHED, bool PAGED>
 __global__ __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(MXFA_VALU_WAVES_PER_EU)))
 void split_kv_valu_kernel(KernelArgs a) {
-    using V = Valu<DT, D, RB, HS, HG>;
+    using V = Valu<DT, D, RB, HS, HG, PAGED>;
     __shared__ __attribute__((aligned(16))) typename V::Smem sm;
     drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
                                  bool whole) {
@@ -392,9 +428,13 @@ template <int DT, int D, int RB, int HS, int HG>
 hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
     KernelArgs args = a;
     void *kargs[] = {&args};
-    const void *fn = a.schedule == kBalanced
-        ? (const void *)&split_kv_valu_kernel<DT, D, RB, HS, HG, kBalanced>
-        : (const void *)&split_kv_valu_kernel<DT, D, RB, HS, HG, kFixed>;
+    const bool paged = a.block_table != nullptr;
+    const void *fn =
+        a.schedule == kBalanced
+            ? (paged ? (const void *)&split_kv_valu_kernel<DT, D, RB, HS, HG, kBalanced, true>
+                     : (const void *)&split_kv_valu_kernel<DT, D, RB, HS, HG, kBalanced, false>)
+            : (paged ? (const void *)&split_kv_valu_kernel<DT, D, RB, HS, HG, kFixed, true>
+                     : (const void *)&split_kv_valu_kernel<DT, D, RB, HS, HG, kFixed, false>);
     return hipLaunchKernel(fn, grid, dim3(kWaves * 64), kargs, 0, stream);
 }
 

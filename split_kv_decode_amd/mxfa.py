@@ -20,6 +20,7 @@ PATH_NAMES = {0: "valu", 1: "mfma"}
 
 # every symbol include/mxfa.h declares
 EXPORTS = ("mxfa_fwd_kvcache", "mxfa_fwd_kvcache_ws", "mxfa_workspace_size",
+           "mxfa_fwd_kvcache_paged", "mxfa_fwd_kvcache_paged_ws", "mxfa_workspace_size_paged",
            "mxfa_plan", "mxfa_last_plan", "mxfa_set_timing_events",
            "mxfa_status_string", "mxfa_version")
 
@@ -66,6 +67,12 @@ def lib() -> ctypes.CDLL:
     L.mxfa_fwd_kvcache_ws.restype = ci
     L.mxfa_workspace_size.argtypes = [ci] * 9 + [ctypes.POINTER(sz)]
     L.mxfa_workspace_size.restype = ci
+    L.mxfa_fwd_kvcache_paged.argtypes = [vp] * 7 + [ci] * 10 + [vp]
+    L.mxfa_fwd_kvcache_paged.restype = ci
+    L.mxfa_fwd_kvcache_paged_ws.argtypes = [vp] * 7 + [ci] * 11 + [vp, sz, vp]
+    L.mxfa_fwd_kvcache_paged_ws.restype = ci
+    L.mxfa_workspace_size_paged.argtypes = [ci] * 10 + [ctypes.POINTER(sz)]
+    L.mxfa_workspace_size_paged.restype = ci
     L.mxfa_plan.argtypes = [ci] * 10 + [ctypes.POINTER(Plan)]
     L.mxfa_plan.restype = ci
     L.mxfa_last_plan.argtypes = [ctypes.POINTER(Plan)]
@@ -123,6 +130,17 @@ def workspace_size(B, Hq, Hkv, D, qLen, kv_cap, causal=False, dtype=MXFA_FP16,
                                    int(num_splits), ctypes.byref(n))
     if st != MXFA_OK:
         raise MxfaError(st, "mxfa_workspace_size")
+    return n.value
+
+
+def workspace_size_paged(B, Hq, Hkv, D, qLen, page_size, max_pages, causal=False,
+                         dtype=MXFA_FP16, num_splits=0) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().mxfa_workspace_size_paged(B, Hq, Hkv, D, qLen, page_size, max_pages,
+                                         int(causal), int(dtype), int(num_splits),
+                                         ctypes.byref(n))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_workspace_size_paged")
     return n.value
 
 
@@ -191,4 +209,69 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
                                            ctypes.c_void_p(stream))
     if st != MXFA_OK:
         raise MxfaError(st, "mxfa_fwd_kvcache")
+    return out, lse
+
+
+def fwd_kvcache_paged(q, k_pages, v_pages, block_table, cache_seqlens=None,
+                      causal: bool = False, out=None, lse=None, return_lse: bool = True,
+                      num_splits: int = 0, workspace=None,
+                      stream=None) -> Tuple[object, Optional[object]]:
+    """Decode attention over a paged cache on the current HIP stream.
+
+    q [B, qLen, Hq, D]; k_pages, v_pages [num_pages, page_size, Hkv, D];
+    block_table int32 [B, max_pages] (token j of sequence b is row
+    j % page_size of page block_table[b, j // page_size]); cache_seqlens
+    int32 [B] or None.  Returns (out, lse)."""
+    import torch
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, qLen, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k_pages / v_pages must be [num_pages, page_size, Hkv, D] matching q")
+    if (not isinstance(block_table, torch.Tensor) or block_table.dtype != torch.int32
+            or not block_table.is_cuda or block_table.dim() != 2
+            or block_table.shape[0] != B or not block_table.is_contiguous()):
+        raise ValueError("block_table must be a contiguous int32 GPU tensor [B, max_pages]")
+    max_pages = block_table.shape[1]
+    dt = _dtype_code(q)
+    if cache_seqlens is not None:
+        if (cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda
+                or tuple(cache_seqlens.shape) != (B,) or not cache_seqlens.is_contiguous()):
+            raise ValueError("cache_seqlens must be a contiguous int32 GPU tensor of shape [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, qLen), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, qLen)
+                              or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, qLen]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    args = (ptr(q), ptr(k_pages), ptr(v_pages), ptr(block_table), ptr(cache_seqlens),
+            ptr(out), ptr(lse), B, Hq, Hkv, D, qLen, num_pages, page_size, max_pages,
+            int(bool(causal)), dt)
+    with torch.cuda.device(q.device):
+        if workspace is None and num_splits == 0:
+            st = lib().mxfa_fwd_kvcache_paged(*args, ctypes.c_void_p(stream))
+        else:
+            if workspace is None:
+                need = workspace_size_paged(B, Hq, Hkv, D, qLen, page_size, max_pages, causal,
+                                            dt, num_splits)
+                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+            st = lib().mxfa_fwd_kvcache_paged_ws(*args, int(num_splits), ptr(workspace),
+                                                 workspace.numel() * workspace.element_size(),
+                                                 ctypes.c_void_p(stream))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_fwd_kvcache_paged")
     return out, lse

@@ -114,3 +114,33 @@ def check_rows(inp, out_gpu, lse_gpu, rows, lse_rel=0.0):
     go = np.stack([out_gpu[b, i, h] for (b, h, i) in rows])
     gl = np.array([lse_gpu[b, h, i] for (b, h, i) in rows])
     return compare(go, gl, ref_o, ref_l, w.dtype, lse_rel)
+
+
+def run_gpu_paged(paged, inp, num_splits: int = 0, use_workspace: bool = True,
+                  device="cuda"):
+    """A paged cache (workloads.PagedCache, CPU) with the queries of ``inp``
+    -> (out f64, lse f64, plan dict)."""
+    import split_kv_decode_amd as mx
+    w = inp.workload
+    g = paged.to(device)
+    q = inp.q.to(device)
+    if use_workspace or num_splits:
+        dt = 1 if w.dtype == "bf16" else 0
+        need = mx.workspace_size_paged(w.B, w.Hq, w.Hkv, w.D, w.qLen, paged.page_size,
+                                       paged.block_table.shape[1], w.causal, dt, num_splits)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        out, lse = mx.fwd_kvcache_paged(q, g.k_pages, g.v_pages, g.block_table,
+                                        g.cache_seqlens, w.causal, num_splits=num_splits,
+                                        workspace=ws)
+    else:
+        out, lse = mx.fwd_kvcache_paged(q, g.k_pages, g.v_pages, g.block_table,
+                                        g.cache_seqlens, w.causal)
+    torch.cuda.synchronize()
+    plan = mx.last_plan().as_dict()
+    return to_f64(out), lse.detach().cpu().double().numpy(), plan
+
+
+def oracle_paged(paged, inp):
+    w = inp.workload
+    return oracle.attention_paged(inp.q, paged.k_pages, paged.v_pages, paged.block_table,
+                                  paged.cache_seqlens, w.causal, w.dtype)

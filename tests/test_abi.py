@@ -102,6 +102,47 @@ def test_invalid_arguments_rejected_before_any_hip_call(kw, status):
     assert _call_ws(**kw) == status
 
 
+def _call_paged(ws_entry=False, num_splits=0, **kw):
+    """mxfa_fwd_kvcache_paged(_ws) with fake (never dereferenced) aligned pointers."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, bt=0x60000, sl=0, out=0x40000, lse=0x50000,
+             B=2, Hq=8, Hkv=2, D=128, qLen=1, num_pages=8, page=16, max_pages=4, causal=0,
+             dtype=0)
+    a.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    args = (vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["bt"]), vp(a["sl"]), vp(a["out"]),
+            vp(a["lse"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["qLen"], a["num_pages"],
+            a["page"], a["max_pages"], a["causal"], a["dtype"])
+    if ws_entry:
+        return m.lib().mxfa_fwd_kvcache_paged_ws(*args, num_splits, None, 0, None)
+    return m.lib().mxfa_fwd_kvcache_paged(*args, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=0), INV), (dict(bt=0x60002), INV), (dict(k=0), INV), (dict(q=0), INV),
+    (dict(page=0), INV), (dict(page=-16), INV), (dict(max_pages=-1), INV),
+    (dict(num_pages=-1), INV), (dict(num_pages=0), INV),
+    (dict(page=8), UNS), (dict(page=24), UNS), (dict(page=1), UNS),
+    (dict(page=1 << 17, Hq=64, Hkv=64), UNS),              # one page past 2^30 bytes
+    (dict(page=1 << 20, max_pages=1 << 12), UNS),          # logical capacity past INT_MAX
+    (dict(num_pages=1 << 40 >> 20, page=1 << 20, Hq=64, Hkv=64, max_pages=1), UNS),
+    (dict(D=96), UNS), (dict(Hq=6, Hkv=4), INV), (dict(causal=3), INV), (dict(dtype=5), INV),
+])
+def test_paged_arguments_rejected_before_any_hip_call(kw, status):
+    assert _call_paged(**kw) == status
+    assert _call_paged(ws_entry=True, **kw) == status
+
+
+def test_paged_empty_and_pageless_problems():
+    assert _call_paged(B=0) == mxfa.MXFA_OK
+    assert _call_paged(qLen=0) == mxfa.MXFA_OK
+    assert _call_paged(ws_entry=True, num_splits=-1) == INV
+    n = ctypes.c_size_t()
+    L = m.lib()
+    assert L.mxfa_workspace_size_paged(2, 8, 2, 128, 1, 12, 4, 0, 0, 0, ctypes.byref(n)) == UNS
+    assert L.mxfa_workspace_size_paged(2, 8, 2, 128, 1, 16, -4, 0, 0, 0, ctypes.byref(n)) == INV
+    assert L.mxfa_workspace_size_paged(2, 8, 2, 128, 1, 16, 4, 0, 0, 0, None) == INV
+
+
 def test_empty_problem_is_a_no_op():
     assert _call(B=0) == mxfa.MXFA_OK
     assert _call(qLen=0) == mxfa.MXFA_OK

@@ -212,3 +212,57 @@ def visible_pairs(w: Workload, lengths: List[int]) -> int:
 def flops(w: Workload, lengths: List[int]) -> int:
     """2*D for QK^T plus 2*D for PV per visible (row, key) pair."""
     return 4 * w.D * visible_pairs(w, lengths)
+
+
+@dataclasses.dataclass
+class PagedCache:
+    """A paged copy of a contiguous cache (see ``to_paged``)."""
+    page_size: int
+    k_pages: torch.Tensor          # [num_pages, page_size, Hkv, D]
+    v_pages: torch.Tensor
+    block_table: torch.Tensor      # int32 [B, max_pages]
+    cache_seqlens: torch.Tensor    # int32 [B]
+
+    def to(self, device) -> "PagedCache":
+        return PagedCache(self.page_size, self.k_pages.to(device), self.v_pages.to(device),
+                          self.block_table.to(device), self.cache_seqlens.to(device))
+
+
+def to_paged(inp: Inputs, page_size: int, seed: int = 0, spare_pages: int = 3,
+             poison: bool = True) -> PagedCache:
+    """Scatter the contiguous cache of ``inp`` into a pool of pages.
+
+    Block i of sequence b (its tokens [i * page_size, (i + 1) * page_size))
+    goes to a page drawn from a seeded random permutation of the pool; the
+    pool has ``spare_pages`` extra pages.  max_pages = ceil(kv_cap /
+    page_size).  Pages and page rows that hold no valid token are filled with
+    NaN (``poison``), and the block-table entries past a sequence's last
+    block hold out-of-pool values (-1, num_pages, large), so any read of them
+    shows.  The lengths are the contiguous cache's (kv_cap when it has none),
+    so the logical sequences are the same.  No arithmetic: a data layout."""
+    w = inp.workload
+    P = page_size
+    max_pages = -(-w.kv_cap // P)
+    num_pages = w.B * max_pages + spare_pages
+    g = torch.Generator().manual_seed(10007 * (seed + 1) + P)
+    perm = torch.randperm(num_pages, generator=g)
+    fill = float("nan") if poison else 0.0
+    kp = torch.full((num_pages, P, w.Hkv, w.D), fill, dtype=w.torch_dtype)
+    vp = torch.full((num_pages, P, w.Hkv, w.D), fill, dtype=w.torch_dtype)
+    bt = torch.empty((w.B, max_pages), dtype=torch.int32)
+    junk = torch.tensor([-1, num_pages, 1 << 30], dtype=torch.int32)
+    lens = inp.lengths()
+    for b in range(w.B):
+        n = max(0, min(lens[b], w.kv_cap))
+        nblk = -(-n // P)
+        for i in range(max_pages):
+            if i < nblk:
+                page = int(perm[b * max_pages + i])
+                bt[b, i] = page
+                t0, t1 = i * P, min((i + 1) * P, n)
+                kp[page, : t1 - t0] = inp.k_cache[b, t0:t1]
+                vp[page, : t1 - t0] = inp.v_cache[b, t0:t1]
+            else:
+                bt[b, i] = junk[(b + i) % 3]
+    seqlens = torch.tensor([max(0, min(n, w.kv_cap)) for n in lens], dtype=torch.int32)
+    return PagedCache(P, kp, vp, bt, seqlens)
