@@ -202,6 +202,42 @@ MXFA_API mxfa_status mxfa_workspace_size_paged(int B, int Hq, int Hkv, int D,
                                                int dtype, int num_splits,
                                                size_t *bytes);
 
+/* In-call KV append, then attention.  The MXFlashAttn package page names a
+ * FlashAttention-compatible attention-with-KV-cache entry point (Python API
+ * section) and its sdist README lists paged KV append as verified
+ * (capability matrix); the FlashAttention rule is taken:
+ *     k_new, v_new  [B, new_len, Hkv, D]   this step's keys and values
+ * token t of sequence b is written to cache position cache_seqlens[b] + t
+ * (cache_seqlens clamped to [0, kv_cap]); positions at or past kv_cap are
+ * dropped.  Attention then runs as in mxfa_fwd_kvcache over
+ * min(cache_seqlens[b] + new_len, kv_cap) keys, so the causal mask aligns the
+ * last query row with the last new token when new_len == qLen.
+ * cache_seqlens is required (non-NULL) when new_len > 0 and is not modified;
+ * the caller advances it.  k_cache / v_cache are written in place (the
+ * append kernel runs on `stream` before the attention kernels).  With
+ * qLen == 0 only the cache is updated.  new_len < 0 is MXFA_ERR_INVALID_ARG;
+ * k_new / v_new must be 16-byte aligned.  workspace == NULL: scratch from the
+ * stream-ordered allocator; otherwise as for mxfa_fwd_kvcache_ws (size from
+ * mxfa_workspace_size).  num_splits as for mxfa_fwd_kvcache_ws. */
+MXFA_API mxfa_status mxfa_fwd_kvcache_append(
+    const void *q, void *k_cache, void *v_cache, const void *k_new,
+    const void *v_new, const int32_t *cache_seqlens, void *out, float *lse,
+    int B, int Hq, int Hkv, int D, int qLen, int new_len, int kv_cap,
+    int causal, int dtype, int num_splits, void *workspace,
+    size_t workspace_bytes, void *stream);
+
+/* The same over a paged cache: position pos of sequence b is row
+ * pos % page_size of page block_table[b * max_pages + pos / page_size]
+ * (the block table must already name the pages the new tokens land in);
+ * workspace size from mxfa_workspace_size_paged. */
+MXFA_API mxfa_status mxfa_fwd_kvcache_paged_append(
+    const void *q, void *k_pages, void *v_pages, const int32_t *block_table,
+    const void *k_new, const void *v_new, const int32_t *cache_seqlens,
+    void *out, float *lse, int B, int Hq, int Hkv, int D, int qLen,
+    int new_len, int num_pages, int page_size, int max_pages, int causal,
+    int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+    void *stream);
+
 /* The plan (path, partitioning, grid, scratch size) for a problem on a
  * device with num_cus compute units (num_cus <= 0 means 256, an MI355X).
  * Pure host code: makes no HIP runtime call, so it works without a GPU. */

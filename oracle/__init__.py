@@ -210,6 +210,68 @@ def attention_paged(q, k_pages, v_pages, block_table, cache_seqlens=None,
     return attention(q, k, v, lens, causal, dtype, nthreads, lib_path)
 
 
+def _lens_for_append(cache_seqlens, B: int, cap: int):
+    sl = _seqlens(cache_seqlens, B)
+    if sl is None:
+        raise ValueError("an append needs cache_seqlens")
+    return [max(0, min(int(x), cap)) for x in sl]
+
+
+def append_kv(k_cache, v_cache, k_new, v_new, cache_seqlens):
+    """The cache after an in-call KV append, and the lengths attention sees.
+
+    The MXFlashAttn package page names a FlashAttention-compatible
+    attention-with-KV-cache entry point (Python API section) and its sdist
+    README lists paged KV append (capability matrix); the FlashAttention rule
+    is read: token t of k_new / v_new [B, new_len, Hkv, D] goes to position
+    n_b + t of sequence b (n_b = cache_seqlens[b] clamped to [0, kv_cap]),
+    positions at or past kv_cap are dropped, and attention then sees
+    min(n_b + new_len, kv_cap) keys.  Returns copies (bit patterns) and the
+    lengths; the inputs are not modified."""
+    k, v = _as_u16(k_cache).copy(), _as_u16(v_cache).copy()
+    kn, vn = _as_u16(k_new), _as_u16(v_new)
+    B, cap = k.shape[:2]
+    new_len = kn.shape[1]
+    lens0 = _lens_for_append(cache_seqlens, B, cap)
+    for b in range(B):
+        for t in range(new_len):
+            pos = lens0[b] + t
+            if pos < cap:
+                k[b, pos] = kn[b, t]
+                v[b, pos] = vn[b, t]
+    return k, v, np.asarray([min(n + new_len, cap) for n in lens0], dtype=np.int32)
+
+
+def append_kv_paged(k_pages, v_pages, block_table, k_new, v_new, cache_seqlens):
+    """``append_kv`` for a paged cache (layout as in ``gather_pages``):
+    position pos of sequence b is row pos % P of page block_table[b, pos // P].
+    Returns the updated pool copies and the lengths."""
+    kp, vp = _as_u16(k_pages).copy(), _as_u16(v_pages).copy()
+    kn, vn = _as_u16(k_new), _as_u16(v_new)
+    num_pages, P = kp.shape[:2]
+    try:
+        import torch
+        if isinstance(block_table, torch.Tensor):
+            block_table = block_table.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    bt = np.asarray(block_table, dtype=np.int64)
+    B, max_pages = bt.shape
+    cap = max_pages * P
+    new_len = kn.shape[1]
+    lens0 = _lens_for_append(cache_seqlens, B, cap)
+    for b in range(B):
+        for t in range(new_len):
+            pos = lens0[b] + t
+            if pos < cap:
+                page = int(bt[b, pos // P])
+                if not 0 <= page < num_pages:
+                    raise ValueError(f"block table of sequence {b} names a page outside the pool")
+                kp[page, pos % P] = kn[b, t]
+                vp[page, pos % P] = vn[b, t]
+    return kp, vp, np.asarray([min(n + new_len, cap) for n in lens0], dtype=np.int32)
+
+
 def decode16(bits: np.ndarray, dtype: str, lib_path: str = LIB_PATH) -> np.ndarray:
     """Decode an array of 16-bit patterns to float64 with the oracle's decoder."""
     lib = load(lib_path)

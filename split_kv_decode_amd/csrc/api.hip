@@ -24,6 +24,7 @@ constexpr size_t kWsAlign = 256;
 struct Problem {
     int B, Hq, Hkv, D, qLen, kv_cap, causal, dtype;
     int page_size = 0, max_pages = 0, num_pages = 0;
+    int new_len = 0;          // tokens appended to every sequence before attention
 };
 
 thread_local mxfa_plan_t t_last_plan;
@@ -261,13 +262,11 @@ mxfa_status device_cus(int *cus) {
     return MXFA_OK;
 }
 
-mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seqlens,
-                const int32_t *block_table, void *out, float *lse, const Problem &p,
-                const FullPlan &f, void *ws, hipStream_t stream) {
-    const mxfa_plan_t &pl = f.pub;
+// Kernel arguments that describe the cache and the sequences.
+KernelArgs cache_args(const void *k, const void *v, const int32_t *seqlens,
+                      const int32_t *block_table, const Problem &p) {
     KernelArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.q = q;
     a.k = k;
     a.v = v;
     a.seqlens = seqlens;
@@ -277,6 +276,21 @@ mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seql
         a.num_pages = p.num_pages;
         a.log_page = __builtin_ctz((unsigned)p.page_size);
     }
+    a.B = p.B;
+    a.Hq = p.Hq;
+    a.Hkv = p.Hkv;
+    a.D = p.D;
+    a.kv_cap = p.kv_cap;
+    a.new_len = p.new_len;
+    return a;
+}
+
+mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seqlens,
+                const int32_t *block_table, const void *k_new, const void *v_new, void *out,
+                float *lse, const Problem &p, const FullPlan &f, void *ws, hipStream_t stream) {
+    const mxfa_plan_t &pl = f.pub;
+    KernelArgs a = cache_args(k, v, seqlens, block_table, p);
+    a.q = q;
     a.out = out;
     a.lse = lse;
     if (pl.combine) {
@@ -284,14 +298,9 @@ mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seql
         a.ws_lse = (float *)((char *)ws + f.o_bytes);
         a.ws_cum = f.cum_bytes ? (int *)((char *)ws + f.o_bytes + f.lse_bytes) : nullptr;
     }
-    a.B = p.B;
-    a.Hq = p.Hq;
-    a.Hkv = p.Hkv;
     a.qLen = p.qLen;
-    a.kv_cap = p.kv_cap;
     a.G = p.Hq / p.Hkv;
     a.R = pl.rows;
-    a.D = p.D;
     a.causal = p.causal;
     a.head_block = pl.head_block;
     a.head_blocks = f.head_blocks;
@@ -303,6 +312,8 @@ mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seql
     a.min_share = f.min_share;
     a.qscale = (float)(1.4426950408889634 / std::sqrt((double)p.D));
     const dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z);
+    if (p.new_len > 0 && launch_append(a, k_new, v_new, stream) != hipSuccess)
+        return MXFA_ERR_HIP;
     if (t_ev_before && hipEventRecord(t_ev_before, stream) != hipSuccess) return MXFA_ERR_HIP;
     const hipError_t e = pl.path == MXFA_PATH_MFMA
                              ? launch_split_mfma(a, p.dtype, grid, stream)
@@ -321,9 +332,9 @@ void record(const mxfa_plan_t &pl) {
 // Plan and launch a checked problem.  own_ws: allocate the scratch on the
 // stream (stream-ordered) instead of using the caller's.
 mxfa_status execute(const void *q, const void *k, const void *v, const int32_t *seqlens,
-                    const int32_t *block_table, void *out, float *lse, const Problem &p,
-                    int num_splits, void *workspace, size_t workspace_bytes, bool own_ws,
-                    hipStream_t s) {
+                    const int32_t *block_table, const void *k_new, const void *v_new,
+                    void *out, float *lse, const Problem &p, int num_splits, void *workspace,
+                    size_t workspace_bytes, bool own_ws, hipStream_t s) {
     if (!own_ws && workspace && !aligned(workspace, kWsAlign)) return MXFA_ERR_INVALID_ARG;
     int cus = 0;
     mxfa_status st = device_cus(&cus);
@@ -339,7 +350,7 @@ mxfa_status execute(const void *q, const void *k, const void *v, const int32_t *
     } else if (f.pub.workspace_bytes > 0 && (!workspace || workspace_bytes < f.pub.workspace_bytes)) {
         return MXFA_ERR_WORKSPACE;
     }
-    st = run(q, k, v, seqlens, block_table, out, lse, p, f, ws, s);
+    st = run(q, k, v, seqlens, block_table, k_new, v_new, out, lse, p, f, ws, s);
     if (own_ws && ws && hipFreeAsync(ws, s) != hipSuccess && st == MXFA_OK) st = MXFA_ERR_HIP;
     if (st == MXFA_OK) record(f.pub);
     return st;
@@ -391,8 +402,8 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_ws(const void *q, const void *k_cache, con
     if (B == 0 || qLen == 0) return MXFA_OK;       // nothing to compute
     st = check_pointers(q, k_cache, v_cache, cache_seqlens, out, lse, kv_cap);
     if (st != MXFA_OK) return st;
-    return execute(q, k_cache, v_cache, cache_seqlens, nullptr, out, lse, p, num_splits,
-                   workspace, workspace_bytes, false, (hipStream_t)stream);
+    return execute(q, k_cache, v_cache, cache_seqlens, nullptr, nullptr, nullptr, out, lse, p,
+                   num_splits, workspace, workspace_bytes, false, (hipStream_t)stream);
 }
 
 MXFA_API mxfa_status mxfa_fwd_kvcache(const void *q, const void *k_cache, const void *v_cache,
@@ -405,8 +416,8 @@ MXFA_API mxfa_status mxfa_fwd_kvcache(const void *q, const void *k_cache, const 
     if (B == 0 || qLen == 0) return MXFA_OK;
     st = check_pointers(q, k_cache, v_cache, cache_seqlens, out, lse, kv_cap);
     if (st != MXFA_OK) return st;
-    return execute(q, k_cache, v_cache, cache_seqlens, nullptr, out, lse, p, 0, nullptr, 0,
-                   true, (hipStream_t)stream);
+    return execute(q, k_cache, v_cache, cache_seqlens, nullptr, nullptr, nullptr, out, lse, p,
+                   0, nullptr, 0, true, (hipStream_t)stream);
 }
 
 MXFA_API mxfa_status mxfa_workspace_size_paged(int B, int Hq, int Hkv, int D, int qLen,
@@ -442,8 +453,8 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_paged_ws(
     st = check_pointers(q, k_pages, v_pages, cache_seqlens, out, lse, p.kv_cap);
     if (st != MXFA_OK) return st;
     if (p.kv_cap > 0 && (!block_table || !aligned(block_table, 4))) return MXFA_ERR_INVALID_ARG;
-    return execute(q, k_pages, v_pages, cache_seqlens, block_table, out, lse, p, num_splits,
-                   workspace, workspace_bytes, false, (hipStream_t)stream);
+    return execute(q, k_pages, v_pages, cache_seqlens, block_table, nullptr, nullptr, out, lse,
+                   p, num_splits, workspace, workspace_bytes, false, (hipStream_t)stream);
 }
 
 MXFA_API mxfa_status mxfa_fwd_kvcache_paged(
@@ -459,8 +470,74 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_paged(
     st = check_pointers(q, k_pages, v_pages, cache_seqlens, out, lse, p.kv_cap);
     if (st != MXFA_OK) return st;
     if (p.kv_cap > 0 && (!block_table || !aligned(block_table, 4))) return MXFA_ERR_INVALID_ARG;
-    return execute(q, k_pages, v_pages, cache_seqlens, block_table, out, lse, p, 0, nullptr, 0,
-                   true, (hipStream_t)stream);
+    return execute(q, k_pages, v_pages, cache_seqlens, block_table, nullptr, nullptr, out, lse,
+                   p, 0, nullptr, 0, true, (hipStream_t)stream);
+}
+
+namespace {
+
+// Shared body of the two appending entry points (p already checked).
+mxfa_status fwd_append(const void *q, void *k, void *v, const int32_t *block_table,
+                       const void *k_new, const void *v_new, const int32_t *cache_seqlens,
+                       void *out, float *lse, Problem p, int new_len, int num_splits,
+                       void *workspace, size_t workspace_bytes, hipStream_t s) {
+    if (new_len < 0 || num_splits < 0) return MXFA_ERR_INVALID_ARG;
+    uint64_t x;
+    if (!mul_ok((uint64_t)p.B, (uint64_t)new_len, &x) || !mul_ok(x, (uint64_t)p.Hkv, &x) ||
+        !mul_ok(x, (uint64_t)p.D, &x) || !mul_ok(x, 2, &x) || x > (UINT64_C(1) << 62))
+        return MXFA_ERR_INVALID_ARG;
+    p.new_len = new_len;
+    if (p.B == 0) return MXFA_OK;
+    const bool appends = new_len > 0 && p.kv_cap > 0;
+    if (new_len > 0) {
+        // the positions come from cache_seqlens
+        if (!cache_seqlens || !aligned(cache_seqlens, 4)) return MXFA_ERR_INVALID_ARG;
+        if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))
+            return MXFA_ERR_INVALID_ARG;
+    }
+    if (appends && (!k || !v || !aligned(k, 16) || !aligned(v, 16))) return MXFA_ERR_INVALID_ARG;
+    if (appends && p.page_size > 0 && (!block_table || !aligned(block_table, 4)))
+        return MXFA_ERR_INVALID_ARG;
+    if (p.qLen == 0) {
+        // no query: only the cache update
+        if (!appends) return MXFA_OK;
+        const KernelArgs a = cache_args(k, v, cache_seqlens, block_table, p);
+        return launch_append(a, k_new, v_new, s) == hipSuccess ? MXFA_OK : MXFA_ERR_HIP;
+    }
+    mxfa_status st = check_pointers(q, k, v, cache_seqlens, out, lse, p.kv_cap);
+    if (st != MXFA_OK) return st;
+    if (p.page_size > 0 && p.kv_cap > 0 && (!block_table || !aligned(block_table, 4)))
+        return MXFA_ERR_INVALID_ARG;
+    return execute(q, k, v, cache_seqlens, block_table, k_new, v_new, out, lse, p, num_splits,
+                   workspace, workspace_bytes, workspace == nullptr, s);
+}
+
+}  // namespace
+
+MXFA_API mxfa_status mxfa_fwd_kvcache_append(
+    const void *q, void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+    const int32_t *cache_seqlens, void *out, float *lse, int B, int Hq, int Hkv, int D,
+    int qLen, int new_len, int kv_cap, int causal, int dtype, int num_splits, void *workspace,
+    size_t workspace_bytes, void *stream) {
+    const Problem p{B, Hq, Hkv, D, qLen, kv_cap, causal, dtype};
+    const mxfa_status st = check_problem(p);
+    if (st != MXFA_OK) return st;
+    return fwd_append(q, k_cache, v_cache, nullptr, k_new, v_new, cache_seqlens, out, lse, p,
+                      new_len, num_splits, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+MXFA_API mxfa_status mxfa_fwd_kvcache_paged_append(
+    const void *q, void *k_pages, void *v_pages, const int32_t *block_table,
+    const void *k_new, const void *v_new, const int32_t *cache_seqlens, void *out,
+    float *lse, int B, int Hq, int Hkv, int D, int qLen, int new_len, int num_pages,
+    int page_size, int max_pages, int causal, int dtype, int num_splits, void *workspace,
+    size_t workspace_bytes, void *stream) {
+    Problem p;
+    const mxfa_status st = paged_problem(B, Hq, Hkv, D, qLen, num_pages, page_size, max_pages,
+                                         causal, dtype, &p);
+    if (st != MXFA_OK) return st;
+    return fwd_append(q, k_pages, v_pages, block_table, k_new, v_new, cache_seqlens, out, lse,
+                      p, new_len, num_splits, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 MXFA_API mxfa_status mxfa_last_plan(mxfa_plan_t *plan) {

@@ -1,0 +1,68 @@
+// In-call KV append: the new keys and values of this step are written into
+// the cache before attention reads it.
+//
+// The MXFlashAttn package page names a FlashAttention-compatible entry point
+// for attention with a KV cache (Python API section), and its sdist README
+// lists paged KV append among the verified capabilities (capability matrix);
+// neither gives the rule, so the FlashAttention one is taken: token t of
+// k_new / v_new [B, new_len, Hkv, D] goes to cache position
+// cache_seqlens[b] + t of sequence b (contiguous row, or row pos % page of
+// page block_table[b][pos / page]), and attention then sees
+// cache_seqlens[b] + new_len keys.  Positions at or past kv_cap are dropped.
+//
+// A plain copy: one thread moves 16 bytes of K and 16 bytes of V.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxfa {
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+template <bool PAGED>
+__global__ __launch_bounds__(kAppendThreads)
+void kv_append_kernel(KernelArgs a, const uint16_t *__restrict__ k_new,
+                      const uint16_t *__restrict__ v_new) {
+    const int b = blockIdx.y;
+    const int nch = a.D / 8;                        // 16-byte chunks of a head row
+    const long long idx = (long long)blockIdx.x * kAppendThreads + threadIdx.x;
+    if (idx >= (long long)a.new_len * a.Hkv * nch) return;
+    const int c = (int)(idx % nch);
+    const int h = (int)((idx / nch) % a.Hkv);
+    const int t = (int)(idx / ((long long)nch * a.Hkv));
+    const int n0 = clampi(a.seqlens[b], 0, a.kv_cap);
+    if (t >= a.kv_cap - n0) return;                 // past the capacity: dropped
+    const int pos = n0 + t;
+    size_t row;                                     // token row index in the cache
+    if constexpr (PAGED) {
+        const int pg = clampi(a.block_table[(size_t)b * a.max_pages + (pos >> a.log_page)], 0,
+                              a.num_pages - 1);
+        row = ((size_t)pg << a.log_page) + (pos & ((1 << a.log_page) - 1));
+    } else {
+        row = (size_t)b * a.kv_cap + pos;
+    }
+    const size_t src = (((size_t)b * a.new_len + t) * a.Hkv + h) * a.D + 8 * c;
+    const size_t dst = (row * a.Hkv + h) * a.D + 8 * c;
+    *(u32x4 *)((uint16_t *)a.k + dst) = *(const u32x4 *)(k_new + src);
+    *(u32x4 *)((uint16_t *)a.v + dst) = *(const u32x4 *)(v_new + src);
+}
+
+}  // namespace
+
+hipError_t launch_append(const KernelArgs &a, const void *k_new, const void *v_new,
+                         hipStream_t stream) {
+    const long long per_seq = (long long)a.new_len * a.Hkv * (a.D / 8);
+    if (per_seq == 0 || a.B == 0 || a.kv_cap == 0) return hipSuccess;
+    const long long blocks = (per_seq + kAppendThreads - 1) / kAppendThreads;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    KernelArgs args = a;
+    const uint16_t *kn = (const uint16_t *)k_new;
+    const uint16_t *vn = (const uint16_t *)v_new;
+    void *kargs[] = {&args, &kn, &vn};
+    const void *fn = a.block_table ? (const void *)&kv_append_kernel<true>
+                                   : (const void *)&kv_append_kernel<false>;
+    return hipLaunchKernel(fn, dim3((unsigned)blocks, a.B), dim3(kAppendThreads), kargs, 0,
+                           stream);
+}
+
+}  // namespace mxfa

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void combine_kernel(KernelArgs 
     const int jst = hb * a.row_blocks + rb;     // stream index within sequence b
     const int st = b * HR + jst;
 
-    const int n = clampi(a.seqlens ? a.seqlens[b] : a.kv_cap, 0, a.kv_cap);
+    const int n = seq_len(a, b);
     long long first;
     int count;
     if (a.schedule == kFixed) {

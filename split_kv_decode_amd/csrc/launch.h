@@ -41,6 +41,7 @@ struct KernelArgs {
     const int32_t *block_table;
     int max_pages, num_pages;
     int log_page;             // log2(page), page a power of two >= kMinPage
+    int new_len;              // tokens appended to every sequence by this call
     void *out;                // [B, qLen, Hq, D]
     float *lse;               // [B, Hq, qLen] or nullptr
     float *ws_o;              // [slots][head_block][row_block][D]
@@ -69,6 +70,15 @@ constexpr int kMinPage = 16;
 // kept in LDS by every workgroup).
 constexpr int kMaxBalancedBatch = 1024;
 
+// Valid length of sequence b for this call: cache_seqlens[b] (kv_cap without
+// them) clamped to [0, kv_cap], plus the tokens appended in the call, at most
+// kv_cap.
+__device__ __forceinline__ int seq_len(const KernelArgs &a, int b) {
+    const int n0 = a.seqlens ? a.seqlens[b] : a.kv_cap;
+    const int n = n0 < 0 ? 0 : (n0 > a.kv_cap ? a.kv_cap : n0);
+    return a.new_len > a.kv_cap - n ? a.kv_cap : n + a.new_len;
+}
+
 hipError_t launch_split_valu(const KernelArgs &a, int dtype, int layout, dim3 grid,
                              hipStream_t stream);
 
@@ -76,6 +86,11 @@ hipError_t launch_split_valu(const KernelArgs &a, int dtype, int layout, dim3 gr
 hipError_t launch_split_mfma(const KernelArgs &a, int dtype, dim3 grid, hipStream_t stream);
 
 hipError_t launch_combine(const KernelArgs &a, int dtype, hipStream_t stream);
+
+// Writes k_new / v_new [B, new_len, Hkv, D] into the cache (contiguous or
+// paged, as described by a) at positions cache_seqlens[b] + t below kv_cap.
+hipError_t launch_append(const KernelArgs &a, const void *k_new, const void *v_new,
+                         hipStream_t stream);
 
 // Query rows per kv head from which the matrix-core path is used.
 constexpr int kMfmaMinRows = 32;

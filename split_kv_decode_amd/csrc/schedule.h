@@ -44,7 +44,7 @@ __device__ __forceinline__ void length_prefix_sums(const KernelArgs &a, long lon
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int bb = t * PER + j;
-        v[j] = bb < a.B ? clampi(a.seqlens ? a.seqlens[bb] : a.kv_cap, 0, a.kv_cap) : 0;
+        v[j] = bb < a.B ? seq_len(a, bb) : 0;
         mine += v[j];
     }
     // inclusive scan of `mine` across the wave
@@ -76,7 +76,7 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         const int split = blockIdx.x;
         const int y = blockIdx.y;
         const int b = blockIdx.z;
-        const int n = clampi(a.seqlens ? a.seqlens[b] : a.kv_cap, 0, a.kv_cap);
+        const int n = seq_len(a, b);
         const int t_lo = split * a.chunk;
         if (split > 0 && t_lo >= n) return;   // partition past this sequence
         const int t_hi = min(t_lo + a.chunk, n);

@@ -21,6 +21,7 @@ PATH_NAMES = {0: "valu", 1: "mfma"}
 # every symbol include/mxfa.h declares
 EXPORTS = ("mxfa_fwd_kvcache", "mxfa_fwd_kvcache_ws", "mxfa_workspace_size",
            "mxfa_fwd_kvcache_paged", "mxfa_fwd_kvcache_paged_ws", "mxfa_workspace_size_paged",
+           "mxfa_fwd_kvcache_append", "mxfa_fwd_kvcache_paged_append",
            "mxfa_plan", "mxfa_last_plan", "mxfa_set_timing_events",
            "mxfa_status_string", "mxfa_version")
 
@@ -73,6 +74,10 @@ def lib() -> ctypes.CDLL:
     L.mxfa_fwd_kvcache_paged_ws.restype = ci
     L.mxfa_workspace_size_paged.argtypes = [ci] * 10 + [ctypes.POINTER(sz)]
     L.mxfa_workspace_size_paged.restype = ci
+    L.mxfa_fwd_kvcache_append.argtypes = [vp] * 8 + [ci] * 10 + [vp, sz, vp]
+    L.mxfa_fwd_kvcache_append.restype = ci
+    L.mxfa_fwd_kvcache_paged_append.argtypes = [vp] * 9 + [ci] * 12 + [vp, sz, vp]
+    L.mxfa_fwd_kvcache_paged_append.restype = ci
     L.mxfa_plan.argtypes = [ci] * 10 + [ctypes.POINTER(Plan)]
     L.mxfa_plan.restype = ci
     L.mxfa_last_plan.argtypes = [ctypes.POINTER(Plan)]
@@ -274,4 +279,74 @@ def fwd_kvcache_paged(q, k_pages, v_pages, block_table, cache_seqlens=None,
                                                  ctypes.c_void_p(stream))
     if st != MXFA_OK:
         raise MxfaError(st, "mxfa_fwd_kvcache_paged")
+    return out, lse
+
+
+def fwd_kvcache_append(q, k_cache, v_cache, k_new, v_new, cache_seqlens, causal: bool = False,
+                       out=None, lse=None, return_lse: bool = True, num_splits: int = 0,
+                       workspace=None, block_table=None,
+                       stream=None) -> Tuple[object, Optional[object]]:
+    """Write k_new / v_new [B, new_len, Hkv, D] into the cache at
+    cache_seqlens[b] + t, then attend over cache_seqlens + new_len keys.
+
+    Contiguous cache [B, kv_cap, Hkv, D], or with ``block_table`` a paged
+    pool [num_pages, page_size, Hkv, D].  The cache is updated in place;
+    cache_seqlens is not."""
+    import torch
+    paged = block_table is not None
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
+                    ("v_new", v_new)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, qLen, Hq, D = q.shape
+    C0, C1, Hkv, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache must match each other and q's head dim")
+    if not paged and C0 != B:
+        raise ValueError("a contiguous cache must be [B, kv_cap, Hkv, D]")
+    Bn, new_len, Hn, Dn = k_new.shape
+    if (Bn, Hn, Dn) != (B, Hkv, D) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new / v_new must be [B, new_len, Hkv, D]")
+    if (not isinstance(cache_seqlens, torch.Tensor) or cache_seqlens.dtype != torch.int32
+            or not cache_seqlens.is_cuda or tuple(cache_seqlens.shape) != (B,)
+            or not cache_seqlens.is_contiguous()):
+        raise ValueError("cache_seqlens must be a contiguous int32 GPU tensor of shape [B]")
+    if paged and (block_table.dtype != torch.int32 or not block_table.is_cuda
+                  or block_table.dim() != 2 or block_table.shape[0] != B
+                  or not block_table.is_contiguous()):
+        raise ValueError("block_table must be a contiguous int32 GPU tensor [B, max_pages]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, qLen), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, qLen)
+                              or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, qLen]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        if paged:
+            st = lib().mxfa_fwd_kvcache_paged_append(
+                ptr(q), ptr(k_cache), ptr(v_cache), ptr(block_table), ptr(k_new), ptr(v_new),
+                ptr(cache_seqlens), ptr(out), ptr(lse), B, Hq, Hkv, D, qLen, new_len, C0, C1,
+                block_table.shape[1], int(bool(causal)), dt, int(num_splits), ptr(workspace),
+                wsb, ctypes.c_void_p(stream))
+        else:
+            st = lib().mxfa_fwd_kvcache_append(
+                ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_new), ptr(v_new), ptr(cache_seqlens),
+                ptr(out), ptr(lse), B, Hq, Hkv, D, qLen, new_len, C1, int(bool(causal)), dt,
+                int(num_splits), ptr(workspace), wsb, ctypes.c_void_p(stream))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_fwd_kvcache_append")
     return out, lse

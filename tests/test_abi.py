@@ -143,6 +143,45 @@ def test_paged_empty_and_pageless_problems():
     assert L.mxfa_workspace_size_paged(2, 8, 2, 128, 1, 16, 4, 0, 0, 0, None) == INV
 
 
+def _call_append(paged=False, **kw):
+    """mxfa_fwd_kvcache(_paged)_append with fake (never dereferenced) aligned pointers."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, kn=0x70000, vn=0x80000, sl=0x90000,
+             out=0x40000, lse=0x50000, bt=0x60000, B=2, Hq=8, Hkv=2, D=128, qLen=1,
+             new_len=1, cap=64, num_pages=8, page=16, max_pages=4, causal=0, dtype=0,
+             num_splits=0)
+    a.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    if paged:
+        return m.lib().mxfa_fwd_kvcache_paged_append(
+            vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["bt"]), vp(a["kn"]), vp(a["vn"]),
+            vp(a["sl"]), vp(a["out"]), vp(a["lse"]), a["B"], a["Hq"], a["Hkv"], a["D"],
+            a["qLen"], a["new_len"], a["num_pages"], a["page"], a["max_pages"], a["causal"],
+            a["dtype"], a["num_splits"], None, 0, None)
+    return m.lib().mxfa_fwd_kvcache_append(
+        vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["kn"]), vp(a["vn"]), vp(a["sl"]),
+        vp(a["out"]), vp(a["lse"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["qLen"],
+        a["new_len"], a["cap"], a["causal"], a["dtype"], a["num_splits"], None, 0, None)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(new_len=-1), INV), (dict(sl=0), INV), (dict(sl=0x90002), INV),
+    (dict(kn=0), INV), (dict(vn=0), INV), (dict(kn=0x70008), INV),
+    (dict(k=0), INV), (dict(num_splits=-2), INV), (dict(D=80), UNS),
+    (dict(qLen=0, k=0), INV),                    # the cache is still written
+    (dict(new_len=2 ** 30, B=2 ** 15, Hkv=1024, Hq=1024), INV),   # k_new byte size
+])
+def test_append_arguments_rejected_before_any_hip_call(paged, kw, status):
+    assert _call_append(paged=paged, **kw) == status
+
+
+def test_append_empty_problems():
+    assert _call_append(B=0) == mxfa.MXFA_OK
+    assert _call_append(paged=True, B=0) == mxfa.MXFA_OK
+    assert _call_append(qLen=0, new_len=0) == mxfa.MXFA_OK
+    assert _call_append(paged=True, bt=0) == INV
+
+
 def test_empty_problem_is_a_no_op():
     assert _call(B=0) == mxfa.MXFA_OK
     assert _call(qLen=0) == mxfa.MXFA_OK

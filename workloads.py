@@ -229,7 +229,7 @@ class PagedCache:
 
 
 def to_paged(inp: Inputs, page_size: int, seed: int = 0, spare_pages: int = 3,
-             poison: bool = True) -> PagedCache:
+             poison: bool = True, reserve: bool = False) -> PagedCache:
     """Scatter the contiguous cache of ``inp`` into a pool of pages.
 
     Block i of sequence b (its tokens [i * page_size, (i + 1) * page_size))
@@ -239,7 +239,9 @@ def to_paged(inp: Inputs, page_size: int, seed: int = 0, spare_pages: int = 3,
     NaN (``poison``), and the block-table entries past a sequence's last
     block hold out-of-pool values (-1, num_pages, large), so any read of them
     shows.  The lengths are the contiguous cache's (kv_cap when it has none),
-    so the logical sequences are the same.  No arithmetic: a data layout."""
+    so the logical sequences are the same.  ``reserve``: every block below
+    kv_cap gets its own page (for appends), none holds junk.  No arithmetic:
+    a data layout."""
     w = inp.workload
     P = page_size
     max_pages = -(-w.kv_cap // P)
@@ -256,7 +258,9 @@ def to_paged(inp: Inputs, page_size: int, seed: int = 0, spare_pages: int = 3,
         n = max(0, min(lens[b], w.kv_cap))
         nblk = -(-n // P)
         for i in range(max_pages):
-            if i < nblk:
+            if reserve and i >= nblk:
+                bt[b, i] = int(perm[b * max_pages + i])
+            elif i < nblk:
                 page = int(perm[b * max_pages + i])
                 bt[b, i] = page
                 t0, t1 = i * P, min((i + 1) * P, n)
