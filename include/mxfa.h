@@ -238,6 +238,35 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_paged_append(
     int dtype, int num_splits, void *workspace, size_t workspace_bytes,
     void *stream);
 
+/* Packed (variable-length) batch.  The MXFlashAttn package page lists a
+ * flash_attn_varlen_func entry point (Python API section) and its sdist README
+ * a varlen layout (capability matrix), without a layout; the FlashAttention
+ * one is taken:
+ *     q, out        [total_q, Hq, D]      queries of all sequences, packed
+ *     k, v          [total_k, Hkv, D]     keys / values, packed
+ *     cu_seqlens_q,
+ *     cu_seqlens_k  int32 [B + 1]         device offsets: sequence b owns rows
+ *                                         cu[b] .. cu[b + 1] - 1
+ *     lse           float32 [Hq, total_q] (may be NULL)
+ * Sequence b has q_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b] queries and
+ * n_b = cu_seqlens_k[b + 1] - cu_seqlens_k[b] keys; offsets are clamped into
+ * [0, total] and the lengths to max_seqlen_q / max_seqlen_k, which the caller
+ * passes as upper bounds (they size the plan; max_seqlen_k * Hkv * D * 2
+ * must stay below 2^30 bytes).  With causal = 1, query i of sequence b sees
+ * key j iff j <= i + n_b - q_b.  Rows of out past every sequence's queries
+ * are not written.  workspace == NULL: scratch from the stream-ordered
+ * allocator; otherwise at least mxfa_workspace_size(B, Hq, Hkv, D,
+ * max_seqlen_q, max_seqlen_k, causal, dtype, num_splits) bytes. */
+MXFA_API mxfa_status mxfa_fwd_varlen(const void *q, const void *k,
+                                     const void *v,
+                                     const int32_t *cu_seqlens_q,
+                                     const int32_t *cu_seqlens_k, void *out,
+                                     float *lse, int B, int Hq, int Hkv, int D,
+                                     int total_q, int total_k, int max_seqlen_q,
+                                     int max_seqlen_k, int causal, int dtype,
+                                     int num_splits, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* The plan (path, partitioning, grid, scratch size) for a problem on a
  * device with num_cus compute units (num_cus <= 0 means 256, an MI355X).
  * Pure host code: makes no HIP runtime call, so it works without a GPU. */

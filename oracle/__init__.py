@@ -272,6 +272,62 @@ def append_kv_paged(k_pages, v_pages, block_table, k_new, v_new, cache_seqlens):
     return kp, vp, np.asarray([min(n + new_len, cap) for n in lens0], dtype=np.int32)
 
 
+def _int_array(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.int64)
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                     max_seqlen_k: int, causal: bool = False, dtype: Optional[str] = None,
+                     nthreads: int = 0,
+                     lib_path: str = LIB_PATH) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention over a packed batch (q [total_q, Hq, D], k / v [total_k, Hkv,
+    D], offsets [B + 1]): the flash_attn_varlen_func layout the MXFlashAttn
+    package page names (Python API section), read the FlashAttention way.
+
+    Each sequence is placed in a padded batch [B, max_seqlen_q, Hq, D] with
+    its q_b queries in the LAST q_b rows, so the padded problem's bottom-right
+    causal alignment (row i sees key j iff j <= i + n_b - max_seqlen_q) is
+    the sequence's own (query i sees j iff j <= i + n_b - q_b); the output
+    rows are read back from there.  Returns (out [total_q, Hq, D] float64,
+    lse [Hq, total_q] float64); rows outside every sequence stay NaN."""
+    qa, ka, va = _as_u16(q), _as_u16(k), _as_u16(v)
+    total_q, Hq, D = qa.shape
+    total_k, Hkv, _ = ka.shape
+    cq, ck = _int_array(cu_seqlens_q), _int_array(cu_seqlens_k)
+    assert cq.shape == ck.shape and cq.ndim == 1
+    B = cq.shape[0] - 1
+    qpad = np.zeros((B, max_seqlen_q, Hq, D), dtype=np.uint16)
+    kpad = np.zeros((B, max(max_seqlen_k, 1), Hkv, D), dtype=np.uint16)
+    vpad = np.zeros_like(kpad)
+    spans, lens = [], []
+    for b in range(B):
+        q0 = min(max(int(cq[b]), 0), total_q)
+        qb = min(min(max(int(cq[b + 1]), q0), total_q) - q0, max_seqlen_q)
+        k0 = min(max(int(ck[b]), 0), total_k)
+        nb = min(min(max(int(ck[b + 1]), k0), total_k) - k0, max_seqlen_k)
+        qpad[b, max_seqlen_q - qb:] = qa[q0:q0 + qb]
+        kpad[b, :nb] = ka[k0:k0 + nb]
+        vpad[b, :nb] = va[k0:k0 + nb]
+        spans.append((q0, qb))
+        lens.append(nb)
+    code = {FP16: "fp16", BF16: "bf16"}[_dtype_code(q, dtype)]
+    o, l = attention(qpad, kpad, vpad, np.asarray(lens, dtype=np.int32), causal, code,
+                     nthreads, lib_path)
+    out = np.full((total_q, Hq, D), np.nan)
+    lse = np.full((Hq, total_q), np.nan)
+    for b, (q0, qb) in enumerate(spans):
+        if qb:
+            out[q0:q0 + qb] = o[b, max_seqlen_q - qb:]
+            lse[:, q0:q0 + qb] = l[b, :, max_seqlen_q - qb:]
+    return out, lse
+
+
 def decode16(bits: np.ndarray, dtype: str, lib_path: str = LIB_PATH) -> np.ndarray:
     """Decode an array of 16-bit patterns to float64 with the oracle's decoder."""
     lib = load(lib_path)

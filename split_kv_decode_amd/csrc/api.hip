@@ -25,6 +25,10 @@ struct Problem {
     int B, Hq, Hkv, D, qLen, kv_cap, causal, dtype;
     int page_size = 0, max_pages = 0, num_pages = 0;
     int new_len = 0;          // tokens appended to every sequence before attention
+    // packed batch: cu_q / cu_k offsets on the device, qLen / kv_cap the
+    // largest lengths
+    const int32_t *cu_q = nullptr, *cu_k = nullptr;
+    int total_q = 0, total_k = 0;
 };
 
 thread_local mxfa_plan_t t_last_plan;
@@ -282,6 +286,10 @@ KernelArgs cache_args(const void *k, const void *v, const int32_t *seqlens,
     a.D = p.D;
     a.kv_cap = p.kv_cap;
     a.new_len = p.new_len;
+    a.cu_q = p.cu_q;
+    a.cu_k = p.cu_k;
+    a.total_q = p.total_q;
+    a.total_k = p.total_k;
     return a;
 }
 
@@ -538,6 +546,37 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_paged_append(
     if (st != MXFA_OK) return st;
     return fwd_append(q, k_pages, v_pages, block_table, k_new, v_new, cache_seqlens, out, lse,
                       p, new_len, num_splits, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+MXFA_API mxfa_status mxfa_fwd_varlen(const void *q, const void *k, const void *v,
+                                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                     void *out, float *lse, int B, int Hq, int Hkv, int D,
+                                     int total_q, int total_k, int max_seqlen_q,
+                                     int max_seqlen_k, int causal, int dtype, int num_splits,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_splits < 0)
+        return MXFA_ERR_INVALID_ARG;
+    Problem p{B, Hq, Hkv, D, max_seqlen_q, max_seqlen_k, causal, dtype};
+    mxfa_status st = check_problem(p);
+    if (st != MXFA_OK) return st;
+    uint64_t x;
+    if (!mul_ok((uint64_t)total_q, (uint64_t)Hq, &x) || !mul_ok(x, (uint64_t)D * 8, &x) ||
+        x > (UINT64_C(1) << 62) || !mul_ok((uint64_t)total_k, (uint64_t)Hkv, &x) ||
+        !mul_ok(x, (uint64_t)D * 2, &x) || x > (UINT64_C(1) << 62))
+        return MXFA_ERR_INVALID_ARG;
+    if (B == 0 || max_seqlen_q == 0 || total_q == 0) return MXFA_OK;
+    if (!cu_seqlens_q || !cu_seqlens_k || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+        return MXFA_ERR_INVALID_ARG;
+    // keys exist only when both the pool and the longest sequence are non-empty
+    st = check_pointers(q, k, v, nullptr, out, lse,
+                        total_k > 0 && max_seqlen_k > 0 ? max_seqlen_k : 0);
+    if (st != MXFA_OK) return st;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    return execute(q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, p, num_splits,
+                   workspace, workspace_bytes, workspace == nullptr, (hipStream_t)stream);
 }
 
 MXFA_API mxfa_status mxfa_last_plan(mxfa_plan_t *plan) {

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void combine_kernel(KernelArgs 
     const int i = (int)(row % a.qLen);
     const int h = (int)((row / a.qLen) % a.Hq);
     const int b = (int)(row / ((long long)a.qLen * a.Hq));
+    if (i >= q_count(a, b)) return;             // past a packed sequence's queries
     const int kvh = h / a.G;
     const int rg = i * a.G + h % a.G;           // row index within the kv head
     const int hb = kvh / a.head_block, hx = kvh % a.head_block;
@@ -127,11 +128,11 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void combine_kernel(KernelArgs 
     const bool empty = !(L > 0.f);
     const float inv = empty ? 0.f : 1.f / L;
     if (g == 0) {
-        uint16_t *outp = (uint16_t *)a.out + (((size_t)b * a.qLen + i) * a.Hq + h) * D + d0;
+        uint16_t *outp = (uint16_t *)a.out + (q_token(a, b, i) * a.Hq + h) * D + d0;
         *(u32x2 *)outp = u32x2{pack2<DT>(acc[0] * inv, acc[1] * inv),
                                pack2<DT>(acc[2] * inv, acc[3] * inv)};
     }
-    if (lane == 0 && a.lse) a.lse[row] = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
+    if (lane == 0 && a.lse) a.lse[lse_index(a, b, h, i)] = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
 }
 
 template <int DT, int D>

@@ -42,6 +42,13 @@ struct KernelArgs {
     int max_pages, num_pages;
     int log_page;             // log2(page), page a power of two >= kMinPage
     int new_len;              // tokens appended to every sequence by this call
+    // Packed (varlen) batches: sequence b's queries are rows cu_q[b] ..
+    // cu_q[b + 1] - 1 of q / out [total_q, Hq, D] (lse [Hq, total_q]) and its
+    // keys rows cu_k[b] .. cu_k[b + 1] - 1 of k / v [total_k, Hkv, D]; qLen
+    // and kv_cap are then the largest lengths.  nullptr: padded layouts.
+    const int32_t *cu_q;
+    const int32_t *cu_k;
+    int total_q, total_k;
     void *out;                // [B, qLen, Hq, D]
     float *lse;               // [B, Hq, qLen] or nullptr
     float *ws_o;              // [slots][head_block][row_block][D]
@@ -70,13 +77,45 @@ constexpr int kMinPage = 16;
 // kept in LDS by every workgroup).
 constexpr int kMaxBalancedBatch = 1024;
 
+__device__ __forceinline__ int clamp_to(int x, int lo, int hi) {
+    return x < lo ? lo : (x > hi ? hi : x);
+}
+
 // Valid length of sequence b for this call: cache_seqlens[b] (kv_cap without
 // them) clamped to [0, kv_cap], plus the tokens appended in the call, at most
-// kv_cap.
+// kv_cap; packed keys: cu_k[b + 1] - cu_k[b], offsets clamped into
+// [0, total_k] and the length to kv_cap.
 __device__ __forceinline__ int seq_len(const KernelArgs &a, int b) {
+    if (a.cu_k) {
+        const int lo = clamp_to(a.cu_k[b], 0, a.total_k);
+        const int hi = clamp_to(a.cu_k[b + 1], lo, a.total_k);
+        return hi - lo < a.kv_cap ? hi - lo : a.kv_cap;
+    }
     const int n0 = a.seqlens ? a.seqlens[b] : a.kv_cap;
-    const int n = n0 < 0 ? 0 : (n0 > a.kv_cap ? a.kv_cap : n0);
+    const int n = clamp_to(n0, 0, a.kv_cap);
     return a.new_len > a.kv_cap - n ? a.kv_cap : n + a.new_len;
+}
+
+// First key row of sequence b in k / v (token rows of Hkv * D values).
+__device__ __forceinline__ size_t kv_token0(const KernelArgs &a, int b) {
+    return a.cu_k ? (size_t)clamp_to(a.cu_k[b], 0, a.total_k) : (size_t)b * a.kv_cap;
+}
+
+// Query rows of sequence b (qLen, or its packed count, at most qLen).
+__device__ __forceinline__ int q_count(const KernelArgs &a, int b) {
+    if (!a.cu_q) return a.qLen;
+    const int lo = clamp_to(a.cu_q[b], 0, a.total_q);
+    const int hi = clamp_to(a.cu_q[b + 1], lo, a.total_q);
+    return hi - lo < a.qLen ? hi - lo : a.qLen;
+}
+
+// Token row of query i of sequence b in q / out, and the lse entry of (b, h, i).
+__device__ __forceinline__ size_t q_token(const KernelArgs &a, int b, int i) {
+    return a.cu_q ? (size_t)clamp_to(a.cu_q[b], 0, a.total_q) + i : (size_t)b * a.qLen + i;
+}
+__device__ __forceinline__ size_t lse_index(const KernelArgs &a, int b, int h, int i) {
+    return a.cu_q ? (size_t)h * a.total_q + q_token(a, b, i)
+                  : ((size_t)b * a.Hq + h) * a.qLen + i;
 }
 
 hipError_t launch_split_valu(const KernelArgs &a, int dtype, int layout, dim3 grid,

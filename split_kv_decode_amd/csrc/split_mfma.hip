@@ -145,11 +145,16 @@ struct Mfma {
         const int g = lane >> 4;
         const int p = lane & 15;
 
-        // keys past t_end are invisible to every row of the block
+        // this sequence's query rows (fewer than R in a packed batch); keys
+        // past t_end are invisible to every row of the block
+        const int qn = __builtin_amdgcn_readfirstlane(q_count(a, b));
+        const int Rb = a.G * qn;
         int t_end = t_hi;
-        if (a.causal) {
-            const int i_max = (min(rb * RB + RB, a.R) - 1) / a.G;
-            t_end = min(t_end, i_max + n - a.qLen + 1);
+        if (rb * RB >= Rb) {
+            t_end = t_lo;               // a row block with no query: nothing to read
+        } else if (a.causal) {
+            const int i_max = (min(rb * RB + RB, Rb) - 1) / a.G;
+            t_end = min(t_end, i_max + n - qn + 1);
             t_end = max(t_end, t_lo);   // an empty segment, never a negative range
         }
         t_end = __builtin_amdgcn_readfirstlane(t_end);
@@ -165,16 +170,16 @@ struct Mfma {
 #pragma unroll
         for (int rt = 0; rt < kRowTiles; ++rt) {
             const int row = rb * RB + rt * 16 + p;
-            const bool ok = row < a.R;
+            const bool ok = row < Rb;
             const int qi = ok ? row / a.G : 0;
             const int qh = kvh * a.G + (ok ? row % a.G : 0);
-            klim[rt] = (a.causal && ok) ? min(t_end - 1, qi + n - a.qLen) : t_end - 1;
+            klim[rt] = (a.causal && ok) ? min(t_end - 1, qi + n - qn) : t_end - 1;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 u32x4 x = {0, 0, 0, 0};
                 if (ok)
                     x = *(const u32x4 *)((const uint16_t *)a.q +
-                                         (((size_t)b * a.qLen + qi) * a.Hq + qh) * D + 32 * kk + 8 * g);
+                                         (q_token(a, b, qi) * a.Hq + qh) * D + 32 * kk + 8 * g);
                 qf[rt][kk] = __builtin_bit_cast(vec, x);
             }
         }
@@ -182,7 +187,7 @@ struct Mfma {
         // K/V of sequence b; the descriptor range ends with token t_end - 1,
         // so loads past it return zeros without touching memory
         const uint32_t tok_bytes = (uint32_t)a.Hkv * D * 2;
-        const size_t seq_off = (size_t)b * a.kv_cap * a.Hkv * D;
+        const size_t seq_off = kv_token0(a, b) * a.Hkv * D;
         const uint32_t range = (uint32_t)t_end * tok_bytes;
         const __amdgpu_buffer_rsrc_t krsrc =
             make_rsrc((const uint16_t *)a.k + (PAGED ? 0 : seq_off), range);
@@ -414,21 +419,21 @@ struct Mfma {
 
         // epilogue: the lane's row, channels 16 db + 4 g .. + 3
         const int row = rb * RB + rloc;
-        if (row < a.R) {
+        if (row < Rb) {
             const int qi = row / a.G;
             const int qh = kvh * a.G + row % a.G;
             const bool empty = !(L > 0.f);
             const float inv = empty ? 0.f : 1.f / L;
             const float lse2 = empty ? kNegInf : M + fast_log2(L);
             if (whole) {
-                uint16_t *op = (uint16_t *)a.out + (((size_t)b * a.qLen + qi) * a.Hq + qh) * D;
+                uint16_t *op = (uint16_t *)a.out + (q_token(a, b, qi) * a.Hq + qh) * D;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
                     *(u32x2 *)(op + 16 * db + 4 * g) =
                         u32x2{pack2<DT>(acc[db][0] * inv, acc[db][1] * inv),
                               pack2<DT>(acc[db][2] * inv, acc[db][3] * inv)};
                 if (g == 0 && a.lse)
-                    a.lse[((size_t)b * a.Hq + qh) * a.qLen + qi] = empty ? kNegInf : lse2 * kLn2;
+                    a.lse[lse_index(a, b, qh, qi)] = empty ? kNegInf : lse2 * kLn2;
             } else {
                 const size_t e = (size_t)slot * RB + rloc;   // head_block = 1
 #pragma unroll

@@ -174,10 +174,15 @@ struct Valu {
         const bool head_ok = kvh < a.Hkv;
 
         const int row0 = rb * RB;
-        if (a.causal) {
-            // no row of this block sees a key past (last query position) + n - qLen
-            const int i_max = (min(row0 + RB, a.R) - 1) / a.G;
-            t_hi = min(t_hi, i_max + n - a.qLen + 1);
+        // this sequence's query rows (fewer than R in a packed batch)
+        const int qn = __builtin_amdgcn_readfirstlane(q_count(a, b));
+        const int Rb = a.G * qn;
+        if (row0 >= Rb) {
+            t_hi = t_lo;                // a row block with no query: nothing to read
+        } else if (a.causal) {
+            // no row of this block sees a key past (last query position) + n - qn
+            const int i_max = (min(row0 + RB, Rb) - 1) / a.G;
+            t_hi = min(t_hi, i_max + n - qn + 1);
             t_hi = max(t_hi, t_lo);     // an empty segment, never a negative range
         }
         // first token of step 0: a paged cache is read in page-aligned steps
@@ -192,19 +197,19 @@ struct Valu {
 
         // the score this lane finishes with belongs to row (row0 + phir)
         const int my_row = row0 + phir;
-        const bool row_ok = head_ok && my_row < a.R;
-        const int causal_last = a.causal ? my_row / a.G + n - a.qLen : INT32_MAX;
+        const bool row_ok = head_ok && my_row < Rb;
+        const int causal_last = a.causal ? my_row / a.G + n - qn : INT32_MAX;
 
         // Q rows of this lane's head, resident for the whole segment (16-bit)
         u32x4 qr[RB];
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int row = row0 + (r ^ phir);
-            if (head_ok && row < a.R) {
+            if (head_ok && row < Rb) {
                 const int i = row / a.G;
                 const int h = kvh * a.G + row % a.G;
                 const uint16_t *qp = (const uint16_t *)a.q +
-                                     (((size_t)b * a.qLen + i) * a.Hq + h) * D + 8 * sl;
+                                     (q_token(a, b, i) * a.Hq + h) * D + 8 * sl;
                 qr[r] = *(const u32x4 *)qp;
             } else {
                 qr[r] = u32x4{0, 0, 0, 0};
@@ -217,7 +222,7 @@ struct Valu {
         // touching memory, so every load is issued unconditionally.  Lanes of
         // a head past Hkv get an offset beyond any valid range (< 2^30).
         const uint32_t tok_bytes = (uint32_t)a.Hkv * D * 2;
-        const size_t seq_off = (size_t)b * a.kv_cap * a.Hkv * D;
+        const size_t seq_off = kv_token0(a, b) * a.Hkv * D;
         const uint32_t range = (uint32_t)t_hi * tok_bytes;
         const __amdgpu_buffer_rsrc_t krsrc =
             make_rsrc((const uint16_t *)a.k + (PAGED ? 0 : seq_off), range);
@@ -374,7 +379,7 @@ struct Valu {
             const int hx = idx / (Q4 * RB);
             const int row = row0 + r;
             const int head = hb * HPW + hx;
-            if (row >= a.R || head >= a.Hkv) continue;
+            if (row >= Rb || head >= a.Hkv) continue;
             float M = kNegInf;
 #pragma unroll
             for (int s2 = 0; s2 < NSTATE; ++s2) M = fmaxf(M, sm.m[s2][hx][r]);
@@ -396,11 +401,11 @@ struct Valu {
             if (whole) {
                 const int i = row / a.G;
                 const int h = head * a.G + row % a.G;
-                uint16_t *op = (uint16_t *)a.out + (((size_t)b * a.qLen + i) * a.Hq + h) * D + d0;
+                uint16_t *op = (uint16_t *)a.out + (q_token(a, b, i) * a.Hq + h) * D + d0;
                 *(u32x2 *)op = u32x2{pack2<DT>(num[0] * inv, num[1] * inv),
                                      pack2<DT>(num[2] * inv, num[3] * inv)};
                 if (d0 == 0 && a.lse)
-                    a.lse[((size_t)b * a.Hq + h) * a.qLen + i] = empty ? kNegInf : lse2 * kLn2;
+                    a.lse[lse_index(a, b, h, i)] = empty ? kNegInf : lse2 * kLn2;
             } else {
                 const size_t e = ((size_t)slot * HPW + hx) * RB + r;
                 *(f32x4 *)(a.ws_o + e * D + d0) =

@@ -21,7 +21,7 @@ PATH_NAMES = {0: "valu", 1: "mfma"}
 # every symbol include/mxfa.h declares
 EXPORTS = ("mxfa_fwd_kvcache", "mxfa_fwd_kvcache_ws", "mxfa_workspace_size",
            "mxfa_fwd_kvcache_paged", "mxfa_fwd_kvcache_paged_ws", "mxfa_workspace_size_paged",
-           "mxfa_fwd_kvcache_append", "mxfa_fwd_kvcache_paged_append",
+           "mxfa_fwd_kvcache_append", "mxfa_fwd_kvcache_paged_append", "mxfa_fwd_varlen",
            "mxfa_plan", "mxfa_last_plan", "mxfa_set_timing_events",
            "mxfa_status_string", "mxfa_version")
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.mxfa_fwd_kvcache_append.restype = ci
     L.mxfa_fwd_kvcache_paged_append.argtypes = [vp] * 9 + [ci] * 12 + [vp, sz, vp]
     L.mxfa_fwd_kvcache_paged_append.restype = ci
+    L.mxfa_fwd_varlen.argtypes = [vp] * 7 + [ci] * 11 + [vp, sz, vp]
+    L.mxfa_fwd_varlen.restype = ci
     L.mxfa_plan.argtypes = [ci] * 10 + [ctypes.POINTER(Plan)]
     L.mxfa_plan.restype = ci
     L.mxfa_last_plan.argtypes = [ctypes.POINTER(Plan)]
@@ -349,4 +351,57 @@ def fwd_kvcache_append(q, k_cache, v_cache, k_new, v_new, cache_seqlens, causal:
                 int(num_splits), ptr(workspace), wsb, ctypes.c_void_p(stream))
     if st != MXFA_OK:
         raise MxfaError(st, "mxfa_fwd_kvcache_append")
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+               causal: bool = False, out=None, lse=None, return_lse: bool = True,
+               num_splits: int = 0, workspace=None,
+               stream=None) -> Tuple[object, Optional[object]]:
+    """Attention over a packed batch: q [total_q, Hq, D], k / v [total_k, Hkv, D],
+    cu_seqlens_q / cu_seqlens_k int32 [B + 1] on the GPU.  Returns (out
+    [total_q, Hq, D], lse [Hq, total_q])."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be 3-D")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k / v must be [total_k, Hkv, D] matching q")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_cuda
+                or t.dim() != 1 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor [B + 1]")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.shape[0] < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B + 1]")
+    B = cu_seqlens_q.shape[0] - 1
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)
+                              or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [Hq, total_q]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ptr = lambda t: None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib().mxfa_fwd_varlen(ptr(q), ptr(k), ptr(v), ptr(cu_seqlens_q),
+                                   ptr(cu_seqlens_k), ptr(out), ptr(lse), B, Hq, Hkv, D,
+                                   total_q, total_k, int(max_seqlen_q), int(max_seqlen_k),
+                                   int(bool(causal)), dt, int(num_splits), ptr(workspace),
+                                   wsb, ctypes.c_void_p(stream))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_fwd_varlen")
     return out, lse

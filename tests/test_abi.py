@@ -27,6 +27,22 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def header_arity():
+    """Number of parameters of every function the header declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m_ in re.finditer(r"MXFA_API\s+[\w\s\*]+?\b(mxfa_\w+)\s*\(([^)]*)\)", text):
+        params = m_.group(2).strip()
+        out[m_.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_the_header():
+    L = m.lib()
+    for name, n in header_arity().items():
+        assert len(getattr(L, name).argtypes) == n, name
+
+
 def test_only_declared_symbols_are_exported():
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", mxfa.LIB_PATH],
@@ -180,6 +196,37 @@ def test_append_empty_problems():
     assert _call_append(paged=True, B=0) == mxfa.MXFA_OK
     assert _call_append(qLen=0, new_len=0) == mxfa.MXFA_OK
     assert _call_append(paged=True, bt=0) == INV
+
+
+def _call_varlen(**kw):
+    """mxfa_fwd_varlen with fake (never dereferenced) aligned pointers."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, cq=0x90000, ck=0xA0000, out=0x40000,
+             lse=0x50000, B=2, Hq=8, Hkv=2, D=128, total_q=5, total_k=100, max_q=4,
+             max_k=80, causal=1, dtype=1, num_splits=0)
+    a.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    return m.lib().mxfa_fwd_varlen(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["cq"]),
+                                   vp(a["ck"]), vp(a["out"]), vp(a["lse"]), a["B"], a["Hq"],
+                                   a["Hkv"], a["D"], a["total_q"], a["total_k"], a["max_q"],
+                                   a["max_k"], a["causal"], a["dtype"], a["num_splits"], None, 0,
+                                   None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cq=0), INV), (dict(ck=0), INV), (dict(cq=0x90002), INV), (dict(q=0), INV),
+    (dict(k=0), INV), (dict(out=0x40004), INV), (dict(total_q=-1), INV),
+    (dict(total_k=-1), INV), (dict(max_q=-1), INV), (dict(max_k=-1), INV),
+    (dict(num_splits=-1), INV), (dict(D=32), UNS), (dict(Hq=3), INV),
+    (dict(max_k=1 << 22, Hkv=128, Hq=128), UNS),           # one sequence past 2^30 bytes
+])
+def test_varlen_arguments_rejected_before_any_hip_call(kw, status):
+    assert _call_varlen(**kw) == status
+
+
+def test_varlen_empty_problems():
+    assert _call_varlen(B=0) == mxfa.MXFA_OK
+    assert _call_varlen(total_q=0, q=0, out=0) == mxfa.MXFA_OK
+    assert _call_varlen(max_q=0) == mxfa.MXFA_OK
 
 
 def test_empty_problem_is_a_no_op():
