@@ -146,6 +146,112 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands):
     print(path)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def time_calls(call, steps, warmup, torch, np, mx, stream):
+    """(ms per whole call over exactly `steps` calls, mean split-kernel ms from
+    HIP events recorded around it on its stream)."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t_start) * 1e3 / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for a, b in evs:
+        mx.set_timing_events(a.cuda_event, b.cuda_event)
+        call()
+    mx.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    return ms, float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def bench_varlen(args):
+    """A packed (varlen) workload: attention TFLOP/s of the whole call; the
+    split kernel against the dense bf16/fp16 matrix-core peak."""
+    import numpy as np
+    import torch
+
+    import split_kv_decode_amd as mx
+    import workloads as wl
+
+    w = wl.VARLEN_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, cq, ck = wl.make_varlen_inputs(w)
+    gq, gk, gv, gcq, gck = (t.to(dev) for t in (q, k, v, cq, ck))
+    mq, mk = max(w.qlens), max(w.klens)
+    dt = mx.MXFA_BF16 if w.dtype == "bf16" else mx.MXFA_FP16
+    need = mx.workspace_size(w.B, w.Hq, w.Hkv, w.D, mq, mk, w.causal, dt, args.num_splits)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(gq)
+    lse = torch.empty((w.Hq, gq.shape[0]), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        mx.fwd_varlen(gq, gk, gv, gcq, gck, mq, mk, w.causal, out=out, lse=lse,
+                      num_splits=args.num_splits, workspace=ws, stream=stream.cuda_stream)
+
+    ms, split_ms = time_calls(call, args.steps, args.warmup, torch, np, mx, stream)
+    plan = mx.last_plan().as_dict()
+    fl = wl.varlen_flops(w)
+    tflops = fl / (ms * 1e-3) / 1e12
+    split_tflops = fl / (split_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # bounded sample: sequence 2 alone (its q chunk against its keys)
+        b = 2
+        sub = wl.VarlenWorkload(w.name, (w.qlens[b],), (w.klens[b],), w.Hq, w.Hkv, w.D,
+                                w.dtype, w.causal, w.sigma, w.seed)
+        q0, q1 = int(cq[b]), int(cq[b + 1])
+        k0, k1 = int(ck[b]), int(ck[b + 1])
+        threads = args.cpu_threads or len(os.sched_getaffinity(0))
+        tc = time.perf_counter()
+        oracle.attention_varlen(q[q0:q1], k[k0:k1], v[k0:k1],
+                                [0, q1 - q0], [0, k1 - k0], q1 - q0, k1 - k0, w.causal,
+                                w.dtype, nthreads=threads)
+        cpu_s = time.perf_counter() - tc
+        cpu = {"value": round(wl.varlen_flops(sub) / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": (f"sequence {b} alone ({w.qlens[b]} queries x {w.klens[b]} keys, "
+                          f"{wl.varlen_flops(sub) / 1e9:.1f} GFLOP, {cpu_s:.2f} s)")}
+    rec = {
+        "metric": "packed chunked-prefill attention TFLOP/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "qlens": list(w.qlens),
+                   "klens": list(w.klens), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "causal": w.causal, "kv_layout": "packed", "parallelism": "single GPU"},
+        "gb_per_s": round(wl.varlen_bytes(w) / (ms * 1e-3) / 1e9, 2),
+        "plan": plan,
+        "roofline": {"bound": "mfma", "kernel": SPLIT_KERNEL[plan["path"]],
+                     "achieved": round(split_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(split_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": fl,
+                     "mean_launch_us": round(split_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +289,9 @@ def main():
     import split_kv_decode_amd as mx
     import workloads as wl
 
+    if args.workload in wl.VARLEN_WORKLOADS:
+        bench_varlen(args)
+        return
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -16,7 +16,11 @@ The five workload families follow the shapes the source pages talk about:
   re-test tables; the 15,000-token prompt with max_model_len 16384)
   -> ``qwen3_8b_decode`` and ``qwen3_4b_long_decode``;
 * Llama-70B shaped decode at 32K context (ops-transformer article, measured
-  data section) with a multi-token (qLen 8) draft -> ``llama70b_mtp_decode``.
+  data section) with a multi-token (qLen 8) draft -> ``llama70b_mtp_decode``;
+* a packed batch of Llama-70B shaped chunked-prefill steps (query chunks of
+  128-512 tokens against 4K-32K caches, the varlen entry point the
+  MXFlashAttn package page names) -> ``llama70b_chunked_prefill``
+  (``VARLEN_WORKLOADS``, drawn by ``make_varlen_inputs``).
 
 Recipe (identical on every machine for a given torch version):
 
@@ -270,3 +274,85 @@ def to_paged(inp: Inputs, page_size: int, seed: int = 0, spare_pages: int = 3,
                 bt[b, i] = junk[(b + i) % 3]
     seqlens = torch.tensor([max(0, min(n, w.kv_cap)) for n in lens], dtype=torch.int32)
     return PagedCache(P, kp, vp, bt, seqlens)
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed batch: sequence b has qlens[b] queries and klens[b] keys."""
+    name: str
+    qlens: Tuple[int, ...]
+    klens: Tuple[int, ...]
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    causal: bool
+    sigma: float
+    seed: int
+
+    @property
+    def B(self) -> int:
+        return len(self.qlens)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float16 if self.dtype == "fp16" else torch.bfloat16
+
+    def describe(self) -> str:
+        return (f"packed B={self.B} q lengths {list(self.qlens)} kv lengths "
+                f"{list(self.klens)} Hq={self.Hq} Hkv={self.Hkv} D={self.D} {self.dtype} "
+                f"{'causal(bottom-right)' if self.causal else 'non-causal'} "
+                f"N(0,{self.sigma:g}^2) seed={self.seed}")
+
+
+VARLEN_WORKLOADS: Dict[str, VarlenWorkload] = {
+    "llama70b_chunked_prefill": VarlenWorkload(
+        "llama70b_chunked_prefill", qlens=(512, 512, 256, 128),
+        klens=(8192, 16384, 4096, 32768), Hq=64, Hkv=8, D=128, dtype="bf16", causal=True,
+        sigma=0.5, seed=601),
+}
+
+
+def make_varlen_inputs(w: VarlenWorkload):
+    """(q [total_q, Hq, D], k, v [total_k, Hkv, D], cu_q, cu_k int32 [B + 1]) on
+    the CPU: q first, then K and V of each sequence in order, N(0, sigma^2)
+    rounded to the storage dtype."""
+    g = torch.Generator().manual_seed(w.seed)
+    td = w.torch_dtype
+    q = (torch.randn(sum(w.qlens), w.Hq, w.D, generator=g) * w.sigma).to(td)
+    ks, vs = [], []
+    for n in w.klens:
+        ks.append((torch.randn(n, w.Hkv, w.D, generator=g) * w.sigma).to(td))
+        vs.append((torch.randn(n, w.Hkv, w.D, generator=g) * w.sigma).to(td))
+    cu_q = torch.tensor([0] + list(itertools_accumulate(w.qlens)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(itertools_accumulate(w.klens)), dtype=torch.int32)
+    return q, torch.cat(ks), torch.cat(vs), cu_q, cu_k
+
+
+def itertools_accumulate(xs):
+    tot = 0
+    for x in xs:
+        tot += x
+        yield tot
+
+
+def varlen_visible_pairs(w: VarlenWorkload) -> int:
+    """(query row, key) pairs inside the mask, over all query heads."""
+    tot = 0
+    for qb, n in zip(w.qlens, w.klens):
+        for i in range(qb):
+            last = (i + n - qb) if w.causal else (n - 1)
+            tot += max(0, min(last, n - 1) + 1)
+    return tot * w.Hq
+
+
+def varlen_flops(w: VarlenWorkload) -> int:
+    """2*D for QK^T plus 2*D for PV per visible (row, key) pair."""
+    return 4 * w.D * varlen_visible_pairs(w)
+
+
+def varlen_bytes(w: VarlenWorkload) -> int:
+    """Q, K, V once, out, lse (fp32) and the two offset arrays."""
+    tq, tk = sum(w.qlens), sum(w.klens)
+    return (2 * tq * w.Hq * w.D * 2 + 2 * tk * w.Hkv * w.D * 2 + tq * w.Hq * 4
+            + 2 * (w.B + 1) * 4)
