@@ -37,9 +37,12 @@
  * Arithmetic: 16-bit inputs, fp32 accumulation (as the SmallQ README's
  * algorithm notes prescribe), output rounded to nearest-even.
  *
- * Supported: D in {64, 128} (the head dims verified on the MXFlashAttn
- * package page); any Hq that is a multiple of Hkv; fp16 and bf16.  Other
- * shapes return MXFA_ERR_UNSUPPORTED; nothing falls back silently.
+ * Supported: head dims D that are multiples of 8 up to 256 (the SmallQ
+ * README's support range allows any head dim and was verified at 64, 128,
+ * 256 and the 192 / 128 split of MLA heads; 64 and 128 are the fast paths,
+ * other dims are padded to 192 or 256 inside the matrix-core kernel); any
+ * Hq that is a multiple of Hkv; fp16 and bf16.  Other shapes return
+ * MXFA_ERR_UNSUPPORTED; nothing falls back silently.
  *
  * Ownership and threading: the caller owns every buffer.  The library keeps
  * no pointer after a call returns.  Its only mutable state is the
@@ -266,6 +269,28 @@ MXFA_API mxfa_status mxfa_fwd_varlen(const void *q, const void *k,
                                      int max_seqlen_k, int causal, int dtype,
                                      int num_splits, void *workspace,
                                      size_t workspace_bytes, void *stream);
+
+/* Different head dims for keys and values (the DeepSeek V3 MLA heads the
+ * SmallQ README verifies: K side 192, V side 128): q [B, qLen, Hq, Dk],
+ * k_cache [B, kv_cap, Hkv, Dk], v_cache [B, kv_cap, Hkv, Dv], out
+ * [B, qLen, Hq, Dv]; the scale is 1/sqrt(Dk).  Dk and Dv are multiples of 8
+ * up to 256.  workspace == NULL: scratch from the stream-ordered allocator;
+ * otherwise at least mxfa_workspace_size_dkdv bytes.  Otherwise as
+ * mxfa_fwd_kvcache_ws. */
+MXFA_API mxfa_status mxfa_fwd_kvcache_dkdv(const void *q, const void *k_cache,
+                                           const void *v_cache,
+                                           const int32_t *cache_seqlens,
+                                           void *out, float *lse, int B, int Hq,
+                                           int Hkv, int Dk, int Dv, int qLen,
+                                           int kv_cap, int causal, int dtype,
+                                           int num_splits, void *workspace,
+                                           size_t workspace_bytes, void *stream);
+
+/* Scratch bytes mxfa_fwd_kvcache_dkdv needs (rules as mxfa_workspace_size). */
+MXFA_API mxfa_status mxfa_workspace_size_dkdv(int B, int Hq, int Hkv, int Dk,
+                                              int Dv, int qLen, int kv_cap,
+                                              int causal, int dtype,
+                                              int num_splits, size_t *bytes);
 
 /* The plan (path, partitioning, grid, scratch size) for a problem on a
  * device with num_cus compute units (num_cus <= 0 means 256, an MI355X).

@@ -59,6 +59,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxo_bf16_to_f64.restype = ctypes.c_double
     lib.mxo_attention.argtypes = [u16p, u16p, u16p, i32p] + [ci] * 8 + [f64p, f64p, ci]
     lib.mxo_attention.restype = ci
+    lib.mxo_attention_dkdv.argtypes = [u16p, u16p, u16p, i32p] + [ci] * 9 + [f64p, f64p, ci]
+    lib.mxo_attention_dkdv.restype = ci
     lib.mxo_attention_rows.argtypes = ([u16p, u16p, u16p, i32p] + [ci] * 8 +
                                        [i32p, ci, f64p, f64p, ci])
     lib.mxo_attention_rows.restype = ci
@@ -120,21 +122,24 @@ def _seqlens(cache_seqlens, B: int):
 def attention(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
               dtype: Optional[str] = None, nthreads: int = 0,
               lib_path: str = LIB_PATH) -> Tuple[np.ndarray, np.ndarray]:
-    """Return (out [B,qLen,Hq,D] float64, lse [B,Hq,qLen] float64)."""
+    """Return (out [B,qLen,Hq,Dv] float64, lse [B,Hq,qLen] float64).
+
+    q and k_cache share the head dim Dk; v_cache may have another, Dv."""
     qa, ka, va = _as_u16(q), _as_u16(k_cache), _as_u16(v_cache)
     B, qLen, Hq, D = qa.shape
     Bk, kv_cap, Hkv, Dk = ka.shape
-    assert Bk == B and Dk == D and va.shape == ka.shape
+    Dv = va.shape[3]
+    assert Bk == B and Dk == D and va.shape[:3] == ka.shape[:3]
     sl = _seqlens(cache_seqlens, B)
-    out = np.empty((B, qLen, Hq, D), dtype=np.float64)
+    out = np.empty((B, qLen, Hq, Dv), dtype=np.float64)
     lse = np.empty((B, Hq, qLen), dtype=np.float64)
     lib = load(lib_path)
-    rc = lib.mxo_attention(_ptr(qa, ctypes.c_uint16), _ptr(ka, ctypes.c_uint16),
-                           _ptr(va, ctypes.c_uint16),
-                           None if sl is None else _ptr(sl, ctypes.c_int32),
-                           B, Hq, Hkv, D, qLen, kv_cap, int(bool(causal)),
-                           _dtype_code(q, dtype), _ptr(out, ctypes.c_double),
-                           _ptr(lse, ctypes.c_double), int(nthreads))
+    rc = lib.mxo_attention_dkdv(_ptr(qa, ctypes.c_uint16), _ptr(ka, ctypes.c_uint16),
+                                _ptr(va, ctypes.c_uint16),
+                                None if sl is None else _ptr(sl, ctypes.c_int32),
+                                B, Hq, Hkv, Dk, Dv, qLen, kv_cap, int(bool(causal)),
+                                _dtype_code(q, dtype), _ptr(out, ctypes.c_double),
+                                _ptr(lse, ctypes.c_double), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (rc={rc})")
     return out, lse

@@ -37,6 +37,10 @@
  * Layouts (all contiguous, row-major):
  *   q, out : [B, qLen, Hq, D]      k, v : [B, kv_cap, Hkv, D]
  *   lse    : [B, Hq, qLen]         cache_seqlens : int32 [B]
+ * Keys and values may have different head dims (the SmallQ README's support
+ * range lists DeepSeek V3 MLA heads, K side 192 and V side 128):
+ * mxo_attention_dkdv takes q, k with Dk channels and v, out with Dv; the
+ * scale is then 1/sqrt(Dk), the dimension the dot product runs over.
  *
  * Planted-mistake builds: compiling with -DMXO_MUTANT=k (k >= 1) introduces
  * one deliberate, plausible error so that the test suite can show its pins
@@ -97,7 +101,7 @@ static double decode(uint16_t x, int dtype)
 typedef struct {
     const uint16_t *q, *k, *v;
     const int32_t *seqlens;
-    int B, Hq, Hkv, D, qLen, kv_cap, causal, dtype;
+    int B, Hq, Hkv, Dk, Dv, qLen, kv_cap, causal, dtype;
 } problem_t;
 
 static int valid_len(const problem_t *p, int b)
@@ -108,12 +112,12 @@ static int valid_len(const problem_t *p, int b)
     return n;
 }
 
-/* One output row (b, h, i).  scratch holds kv_cap doubles (scores) plus D
+/* One output row (b, h, i).  scratch holds kv_cap doubles (scores) plus Dk
  * doubles (the decoded query row). */
 static void attend_row(const problem_t *p, int b, int h, int i,
                        double *o_row, double *lse_out, double *scratch)
 {
-    const int D = p->D;
+    const int Dk = p->Dk, Dv = p->Dv;
     const int G = p->Hq / p->Hkv;
 #if MXO_MUTANT == 1
     const int hk = h % p->Hkv;          /* wrong GQA head mapping */
@@ -131,36 +135,36 @@ static void attend_row(const problem_t *p, int b, int h, int i,
         if (c < last) last = c;
     }
     if (last < 0) {                     /* no visible key */
-        for (int d = 0; d < D; ++d) o_row[d] = 0.0;
+        for (int d = 0; d < Dv; ++d) o_row[d] = 0.0;
         *lse_out = -INFINITY;
         return;
     }
     double *s = scratch;
     double *qd = scratch + p->kv_cap;
-    const int64_t qoff = (((int64_t)b * p->qLen + i) * p->Hq + h) * D;
-    for (int d = 0; d < D; ++d) qd[d] = decode(p->q[qoff + d], p->dtype);
+    const int64_t qoff = (((int64_t)b * p->qLen + i) * p->Hq + h) * Dk;
+    for (int d = 0; d < Dk; ++d) qd[d] = decode(p->q[qoff + d], p->dtype);
 
 #if MXO_MUTANT == 3
-    const double scale = 1.0 / (double)D;          /* wrong scale */
+    const double scale = 1.0 / (double)Dk;         /* wrong scale */
 #else
-    const double scale = 1.0 / sqrt((double)D);
+    const double scale = 1.0 / sqrt((double)Dk);
 #endif
     /* Pass 1: scores and their maximum. */
     double m = -INFINITY;
     for (int j = 0; j <= last; ++j) {
-        const int64_t koff = (((int64_t)b * p->kv_cap + j) * p->Hkv + hk) * D;
+        const int64_t koff = (((int64_t)b * p->kv_cap + j) * p->Hkv + hk) * Dk;
         double acc = 0.0;
 #if MXO_MUTANT == 4
-        for (int d = 0; d < D - 1; ++d)            /* dropped last channel */
+        for (int d = 0; d < Dk - 1; ++d)           /* dropped last channel */
 #else
-        for (int d = 0; d < D; ++d)
+        for (int d = 0; d < Dk; ++d)
 #endif
             acc += qd[d] * decode(p->k[koff + d], p->dtype);
         s[j] = scale * acc;
         if (s[j] > m) m = s[j];
     }
     /* Pass 2: softmax weights, their sum and the weighted sum of V rows. */
-    for (int d = 0; d < D; ++d) o_row[d] = 0.0;
+    for (int d = 0; d < Dv; ++d) o_row[d] = 0.0;
     double l = 0.0;
     for (int j = 0; j <= last; ++j) {
 #if MXO_MUTANT == 5
@@ -170,33 +174,34 @@ static void attend_row(const problem_t *p, int b, int h, int i,
 #endif
         const double w = exp(s[j] - m);
         l += w;
-        const int64_t voff = (((int64_t)b * p->kv_cap + jv) * p->Hkv + hk) * D;
-        for (int d = 0; d < D; ++d)
+        const int64_t voff = (((int64_t)b * p->kv_cap + jv) * p->Hkv + hk) * Dv;
+        for (int d = 0; d < Dv; ++d)
             o_row[d] += w * decode(p->v[voff + d], p->dtype);
     }
 #if MXO_MUTANT == 6
     /* forgot to normalise by l */
     *lse_out = m + log(l);
 #elif MXO_MUTANT == 7
-    for (int d = 0; d < D; ++d) o_row[d] /= l;
+    for (int d = 0; d < Dv; ++d) o_row[d] /= l;
     *lse_out = log(l);                              /* dropped the max term */
 #else
-    for (int d = 0; d < D; ++d) o_row[d] /= l;
+    for (int d = 0; d < Dv; ++d) o_row[d] /= l;
     *lse_out = m + log(l);
 #endif
 #if MXO_MUTANT == 8
     /* transposed operand: K and V swapped in the product */
     {
+        const int Dm = Dk < Dv ? Dk : Dv;
         double l2 = 0.0;
-        for (int d = 0; d < D; ++d) o_row[d] = 0.0;
+        for (int d = 0; d < Dv; ++d) o_row[d] = 0.0;
         for (int j = 0; j <= last; ++j) {
             const double w = exp(s[j] - m);
             l2 += w;
-            const int64_t off = (((int64_t)b * p->kv_cap + j) * p->Hkv + hk) * D;
-            for (int d = 0; d < D; ++d)
+            const int64_t off = (((int64_t)b * p->kv_cap + j) * p->Hkv + hk) * Dk;
+            for (int d = 0; d < Dm; ++d)
                 o_row[d] += w * decode(p->k[off + d], p->dtype);
         }
-        for (int d = 0; d < D; ++d) o_row[d] /= l2;
+        for (int d = 0; d < Dv; ++d) o_row[d] /= l2;
     }
 #endif
 }
@@ -204,7 +209,7 @@ static void attend_row(const problem_t *p, int b, int h, int i,
 static int check_args(const problem_t *p)
 {
     if (!p->q || !p->k || !p->v) return 1;
-    if (p->B < 0 || p->qLen < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->D <= 0 ||
+    if (p->B < 0 || p->qLen < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Dk <= 0 || p->Dv <= 0 ||
         p->kv_cap < 0)
         return 1;
     if (p->Hq % p->Hkv) return 1;
@@ -212,15 +217,15 @@ static int check_args(const problem_t *p)
     return 0;
 }
 
-/* Full attention: out [B,qLen,Hq,D] and lse [B,Hq,qLen] in double.
- * nthreads <= 0 lets OpenMP choose.  Returns 0 on success, 1 on bad args,
- * 2 if scratch memory could not be allocated. */
-int mxo_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                  const int32_t *cache_seqlens, int B, int Hq, int Hkv, int D,
-                  int qLen, int kv_cap, int causal, int dtype,
-                  double *out, double *lse, int nthreads)
+/* Full attention with key / value head dims Dk / Dv: out [B,qLen,Hq,Dv] and
+ * lse [B,Hq,qLen] in double.  nthreads <= 0 lets OpenMP choose.  Returns 0
+ * on success, 1 on bad args, 2 if scratch memory could not be allocated. */
+int mxo_attention_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const int32_t *cache_seqlens, int B, int Hq, int Hkv, int Dk,
+                       int Dv, int qLen, int kv_cap, int causal, int dtype,
+                       double *out, double *lse, int nthreads)
 {
-    problem_t p = {q, k, v, cache_seqlens, B, Hq, Hkv, D, qLen, kv_cap,
+    problem_t p = {q, k, v, cache_seqlens, B, Hq, Hkv, Dk, Dv, qLen, kv_cap,
                    causal ? 1 : 0, dtype};
     if (check_args(&p) || !out || !lse) return 1;
     const int64_t nrows = (int64_t)B * Hq * qLen;
@@ -230,7 +235,7 @@ int mxo_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 #pragma omp parallel num_threads(nthreads) reduction(|: fail)
 #endif
     {
-        double *scratch = (double *)malloc(sizeof(double) * ((size_t)kv_cap + D));
+        double *scratch = (double *)malloc(sizeof(double) * ((size_t)kv_cap + Dk));
         if (!scratch) {
             fail = 1;
         } else {
@@ -242,13 +247,23 @@ int mxo_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 const int h = (int)((r / qLen) % Hq);
                 const int b = (int)(r / ((int64_t)qLen * Hq));
                 attend_row(&p, b, h, i,
-                           out + (((int64_t)b * qLen + i) * Hq + h) * D,
+                           out + (((int64_t)b * qLen + i) * Hq + h) * Dv,
                            lse + r, scratch);
             }
             free(scratch);
         }
     }
     return fail ? 2 : 0;
+}
+
+/* Full attention with one head dim D for q, k, v and out. */
+int mxo_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const int32_t *cache_seqlens, int B, int Hq, int Hkv, int D,
+                  int qLen, int kv_cap, int causal, int dtype,
+                  double *out, double *lse, int nthreads)
+{
+    return mxo_attention_dkdv(q, k, v, cache_seqlens, B, Hq, Hkv, D, D, qLen, kv_cap,
+                              causal, dtype, out, lse, nthreads);
 }
 
 /* Selected rows only: rows holds nrows triples (b, h, i); out_rows is
@@ -260,7 +275,7 @@ int mxo_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        const int32_t *rows, int nrows, double *out_rows,
                        double *lse_rows, int nthreads)
 {
-    problem_t p = {q, k, v, cache_seqlens, B, Hq, Hkv, D, qLen, kv_cap,
+    problem_t p = {q, k, v, cache_seqlens, B, Hq, Hkv, D, D, qLen, kv_cap,
                    causal ? 1 : 0, dtype};
     if (check_args(&p) || !rows || nrows < 0 || !out_rows || !lse_rows) return 1;
     for (int r = 0; r < nrows; ++r) {

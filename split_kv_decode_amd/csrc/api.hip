@@ -29,6 +29,11 @@ struct Problem {
     // largest lengths
     const int32_t *cu_q = nullptr, *cu_k = nullptr;
     int total_q = 0, total_k = 0;
+    // head dims of q / k and of v / out when they differ (0: both are D)
+    int Dk = 0, Dv = 0;
+    int dk() const { return Dk ? Dk : D; }
+    int dv() const { return Dv ? Dv : D; }
+    int dmax() const { return dk() > dv() ? dk() : dv(); }
 };
 
 thread_local mxfa_plan_t t_last_plan;
@@ -43,7 +48,8 @@ bool mul_ok(uint64_t a, uint64_t b, uint64_t *out) {
 }
 
 mxfa_status check_problem(const Problem &p) {
-    if (p.B < 0 || p.qLen < 0 || p.kv_cap < 0 || p.Hq <= 0 || p.Hkv <= 0 || p.D <= 0)
+    if (p.B < 0 || p.qLen < 0 || p.kv_cap < 0 || p.Hq <= 0 || p.Hkv <= 0 || p.dk() <= 0 ||
+        p.dv() <= 0)
         return MXFA_ERR_INVALID_ARG;
     if (p.Hq % p.Hkv != 0) return MXFA_ERR_INVALID_ARG;
     if (p.causal != 0 && p.causal != 1) return MXFA_ERR_INVALID_ARG;
@@ -51,29 +57,31 @@ mxfa_status check_problem(const Problem &p) {
     // byte sizes of every tensor must be representable
     uint64_t x;
     if (!mul_ok((uint64_t)p.B, (uint64_t)p.kv_cap, &x) || !mul_ok(x, (uint64_t)p.Hkv, &x) ||
-        !mul_ok(x, (uint64_t)p.D, &x) || !mul_ok(x, 2, &x) || x > (UINT64_C(1) << 62))
+        !mul_ok(x, (uint64_t)p.dmax(), &x) || !mul_ok(x, 2, &x) || x > (UINT64_C(1) << 62))
         return MXFA_ERR_INVALID_ARG;
     if (!mul_ok((uint64_t)p.B, (uint64_t)p.qLen, &x) || !mul_ok(x, (uint64_t)p.Hq, &x) ||
-        !mul_ok(x, (uint64_t)p.D, &x) || !mul_ok(x, 8, &x) || x > (UINT64_C(1) << 62))
+        !mul_ok(x, (uint64_t)p.dmax(), &x) || !mul_ok(x, 8, &x) || x > (UINT64_C(1) << 62))
         return MXFA_ERR_INVALID_ARG;
-    if (p.D != 64 && p.D != 128) return MXFA_ERR_UNSUPPORTED;
+    // head dims: multiples of 8 (16-byte rows) up to 256
+    if (p.dk() % 8 || p.dv() % 8 || p.dk() > 256 || p.dv() > 256) return MXFA_ERR_UNSUPPORTED;
     if (p.B > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
     if (p.page_size > 0) {
         // paged: the pool's byte size must be representable; one page is
         // addressed with 32-bit offsets, so it must stay below 2^30 bytes
         if (!mul_ok((uint64_t)p.num_pages, (uint64_t)p.page_size, &x) ||
-            !mul_ok(x, (uint64_t)p.Hkv, &x) || !mul_ok(x, (uint64_t)p.D, &x) ||
+            !mul_ok(x, (uint64_t)p.Hkv, &x) || !mul_ok(x, (uint64_t)p.dmax(), &x) ||
             !mul_ok(x, 2, &x) || x > (UINT64_C(1) << 62))
             return MXFA_ERR_INVALID_ARG;
-        if ((uint64_t)p.page_size * p.Hkv * p.D * 2 > (UINT64_C(1) << 30))
+        if ((uint64_t)p.page_size * p.Hkv * p.dmax() * 2 > (UINT64_C(1) << 30))
             return MXFA_ERR_UNSUPPORTED;
         return MXFA_OK;
     }
     // K/V are addressed with 32-bit byte offsets inside one sequence; loads
     // issued ahead may run up to 1024 tokens past the cache, so both the
     // cache and that slack must stay below 2^30 bytes
-    if ((uint64_t)p.kv_cap * p.Hkv * p.D * 2 > (UINT64_C(1) << 30)) return MXFA_ERR_UNSUPPORTED;
-    if ((uint64_t)1024 * p.Hkv * p.D * 2 > (UINT64_C(1) << 30)) return MXFA_ERR_UNSUPPORTED;
+    if ((uint64_t)p.kv_cap * p.Hkv * p.dmax() * 2 > (UINT64_C(1) << 30))
+        return MXFA_ERR_UNSUPPORTED;
+    if ((uint64_t)1024 * p.Hkv * p.dmax() * 2 > (UINT64_C(1) << 30)) return MXFA_ERR_UNSUPPORTED;
     return MXFA_OK;
 }
 
@@ -149,6 +157,15 @@ int valu_layout(int Hkv, int D, int *heads_per_block) {
 // partitions.  The SmallQ README derives its KV block from the on-chip buffer
 // size; here the on-chip tile is fixed per kernel and only the work split is
 // planned.
+// Channels per row of the partial outputs: the head dim on the VALU path,
+// the padded V tile width on the matrix-core path.
+int out_tile(const Problem &p, int path) {
+    if (path != MXFA_PATH_MFMA) return p.dv();
+    int tk, tv;
+    mfma_tile_dims(p.dk(), p.dv(), &tk, &tv);
+    return tv;
+}
+
 struct FullPlan {
     mxfa_plan_t pub;
     int head_blocks, row_blocks, min_share;
@@ -172,10 +189,12 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     if (R > INT32_MAX) return MXFA_ERR_UNSUPPORTED;
     pl.rows = (int)R;
     int hpb = 1;
-    if (R >= kMfmaMinRows) {
-        // many rows per kv head: Q K^T and P V are dense 16-row tiles
+    const bool valu_dims = p.dk() == p.dv() && (p.dk() == 64 || p.dk() == 128);
+    if (R >= kMfmaMinRows || !valu_dims) {
+        // many rows per kv head (Q K^T and P V are dense 16-row tiles), or a
+        // head shape only the matrix-core kernel's padded tiles hold
         pl.path = MXFA_PATH_MFMA;
-        pl.row_block = kMfmaRowBlock;
+        pl.row_block = mfma_row_block(p.dk(), p.dv());
         pl.layout = kTokens;
     } else {
         pl.path = MXFA_PATH_VALU;
@@ -234,7 +253,7 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     std::memset(&f, 0, sizeof(f));
     if (pl.combine) {
         const size_t entries = (size_t)slots * hpb * pl.row_block;
-        f.o_bytes = align_up(entries * p.D * sizeof(float));
+        f.o_bytes = align_up(entries * out_tile(p, pl.path) * sizeof(float));
         f.lse_bytes = align_up(entries * sizeof(float));
         f.cum_bytes = pl.schedule == kBalanced ? align_up((size_t)(p.B + 2) * sizeof(long long)) : 0;
         pl.workspace_bytes = f.o_bytes + f.lse_bytes + f.cum_bytes;
@@ -283,7 +302,9 @@ KernelArgs cache_args(const void *k, const void *v, const int32_t *seqlens,
     a.B = p.B;
     a.Hq = p.Hq;
     a.Hkv = p.Hkv;
-    a.D = p.D;
+    a.D = p.dk();
+    a.Dk = p.dk();
+    a.Dv = p.dv();
     a.kv_cap = p.kv_cap;
     a.new_len = p.new_len;
     a.cu_q = p.cu_q;
@@ -318,7 +339,8 @@ mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seql
     a.chunk = pl.chunk;
     a.S = pl.num_splits;
     a.min_share = f.min_share;
-    a.qscale = (float)(1.4426950408889634 / std::sqrt((double)p.D));
+    a.qscale = (float)(1.4426950408889634 / std::sqrt((double)p.dk()));
+    a.dv_tile = out_tile(p, pl.path);
     const dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z);
     if (p.new_len > 0 && launch_append(a, k_new, v_new, stream) != hipSuccess)
         return MXFA_ERR_HIP;
@@ -492,7 +514,7 @@ mxfa_status fwd_append(const void *q, void *k, void *v, const int32_t *block_tab
     if (new_len < 0 || num_splits < 0) return MXFA_ERR_INVALID_ARG;
     uint64_t x;
     if (!mul_ok((uint64_t)p.B, (uint64_t)new_len, &x) || !mul_ok(x, (uint64_t)p.Hkv, &x) ||
-        !mul_ok(x, (uint64_t)p.D, &x) || !mul_ok(x, 2, &x) || x > (UINT64_C(1) << 62))
+        !mul_ok(x, (uint64_t)p.dmax(), &x) || !mul_ok(x, 2, &x) || x > (UINT64_C(1) << 62))
         return MXFA_ERR_INVALID_ARG;
     p.new_len = new_len;
     if (p.B == 0) return MXFA_OK;
@@ -579,6 +601,45 @@ MXFA_API mxfa_status mxfa_fwd_varlen(const void *q, const void *k, const void *v
                    workspace, workspace_bytes, workspace == nullptr, (hipStream_t)stream);
 }
 
+MXFA_API mxfa_status mxfa_workspace_size_dkdv(int B, int Hq, int Hkv, int Dk, int Dv, int qLen,
+                                              int kv_cap, int causal, int dtype, int num_splits,
+                                              size_t *bytes) {
+    if (!bytes || num_splits < 0) return MXFA_ERR_INVALID_ARG;
+    Problem p{B, Hq, Hkv, Dk, qLen, kv_cap, causal, dtype};
+    p.Dk = Dk;
+    p.Dv = Dv;
+    mxfa_status st = check_problem(p);
+    if (st != MXFA_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != MXFA_OK) return st;
+    FullPlan f;
+    st = make_plan(p, num_splits, cus, &f);
+    if (st != MXFA_OK) return st;
+    *bytes = (B == 0 || qLen == 0) ? 0 : f.pub.workspace_bytes;
+    return MXFA_OK;
+}
+
+MXFA_API mxfa_status mxfa_fwd_kvcache_dkdv(const void *q, const void *k_cache,
+                                           const void *v_cache, const int32_t *cache_seqlens,
+                                           void *out, float *lse, int B, int Hq, int Hkv,
+                                           int Dk, int Dv, int qLen, int kv_cap, int causal,
+                                           int dtype, int num_splits, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    Problem p{B, Hq, Hkv, Dk, qLen, kv_cap, causal, dtype};
+    p.Dk = Dk;
+    p.Dv = Dv;
+    mxfa_status st = check_problem(p);
+    if (st != MXFA_OK) return st;
+    if (num_splits < 0) return MXFA_ERR_INVALID_ARG;
+    if (B == 0 || qLen == 0) return MXFA_OK;
+    st = check_pointers(q, k_cache, v_cache, cache_seqlens, out, lse, kv_cap);
+    if (st != MXFA_OK) return st;
+    return execute(q, k_cache, v_cache, cache_seqlens, nullptr, nullptr, nullptr, out, lse, p,
+                   num_splits, workspace, workspace_bytes, workspace == nullptr,
+                   (hipStream_t)stream);
+}
+
 MXFA_API mxfa_status mxfa_last_plan(mxfa_plan_t *plan) {
     if (!plan || !t_has_last) return MXFA_ERR_INVALID_ARG;
     *plan = t_last_plan;
@@ -596,7 +657,9 @@ MXFA_API const char *mxfa_status_string(int status) {
     switch (status) {
     case MXFA_OK: return "MXFA_OK: success";
     case MXFA_ERR_INVALID_ARG: return "MXFA_ERR_INVALID_ARG: invalid argument";
-    case MXFA_ERR_UNSUPPORTED: return "MXFA_ERR_UNSUPPORTED: unsupported shape (D must be 64 or 128)";
+    case MXFA_ERR_UNSUPPORTED:
+        return "MXFA_ERR_UNSUPPORTED: unsupported shape (head dims must be multiples of 8 up to "
+               "256; see mxfa.h for the other limits)";
     case MXFA_ERR_WORKSPACE: return "MXFA_ERR_WORKSPACE: workspace missing or too small";
     case MXFA_ERR_HIP: return "MXFA_ERR_HIP: HIP runtime error";
     default: return "unknown mxfa status";

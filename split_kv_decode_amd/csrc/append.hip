@@ -24,7 +24,8 @@ __global__ __launch_bounds__(kAppendThreads)
 void kv_append_kernel(KernelArgs a, const uint16_t *__restrict__ k_new,
                       const uint16_t *__restrict__ v_new) {
     const int b = blockIdx.y;
-    const int nch = a.D / 8;                        // 16-byte chunks of a head row
+    const int nck = a.Dk / 8, ncv = a.Dv / 8;       // 16-byte chunks of a K / V head row
+    const int nch = nck > ncv ? nck : ncv;
     const long long idx = (long long)blockIdx.x * kAppendThreads + threadIdx.x;
     if (idx >= (long long)a.new_len * a.Hkv * nch) return;
     const int c = (int)(idx % nch);
@@ -41,17 +42,21 @@ void kv_append_kernel(KernelArgs a, const uint16_t *__restrict__ k_new,
     } else {
         row = (size_t)b * a.kv_cap + pos;
     }
-    const size_t src = (((size_t)b * a.new_len + t) * a.Hkv + h) * a.D + 8 * c;
-    const size_t dst = (row * a.Hkv + h) * a.D + 8 * c;
-    *(u32x4 *)((uint16_t *)a.k + dst) = *(const u32x4 *)(k_new + src);
-    *(u32x4 *)((uint16_t *)a.v + dst) = *(const u32x4 *)(v_new + src);
+    const size_t tok = (size_t)b * a.new_len + t;
+    if (c < nck)
+        *(u32x4 *)((uint16_t *)a.k + (row * a.Hkv + h) * a.Dk + 8 * c) =
+            *(const u32x4 *)(k_new + (tok * a.Hkv + h) * a.Dk + 8 * c);
+    if (c < ncv)
+        *(u32x4 *)((uint16_t *)a.v + (row * a.Hkv + h) * a.Dv + 8 * c) =
+            *(const u32x4 *)(v_new + (tok * a.Hkv + h) * a.Dv + 8 * c);
 }
 
 }  // namespace
 
 hipError_t launch_append(const KernelArgs &a, const void *k_new, const void *v_new,
                          hipStream_t stream) {
-    const long long per_seq = (long long)a.new_len * a.Hkv * (a.D / 8);
+    const long long per_seq =
+        (long long)a.new_len * a.Hkv * ((a.Dk > a.Dv ? a.Dk : a.Dv) / 8);
     if (per_seq == 0 || a.B == 0 || a.kv_cap == 0) return hipSuccess;
     const long long blocks = (per_seq + kAppendThreads - 1) / kAppendThreads;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;

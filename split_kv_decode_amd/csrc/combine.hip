@@ -20,7 +20,9 @@
 // with one partition per lane and kept in LDS; the weighted sum then splits
 // the wave into NG groups of D/4 lanes (4 channels per lane, 16-byte loads),
 // each group taking every NG-th partition with UNR loads in flight, and the
-// groups are summed with cross-lane exchanges.
+// groups are summed with cross-lane exchanges.  D here is the channel count
+// of a partial row (the head dim, or the matrix-core kernel's padded V tile);
+// only the first Dv channels are written out.
 #include "device_common.h"
 #include "launch.h"
 
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void combine_kernel(KernelArgs 
 
     const bool empty = !(L > 0.f);
     const float inv = empty ? 0.f : 1.f / L;
-    if (g == 0) {
-        uint16_t *outp = (uint16_t *)a.out + (q_token(a, b, i) * a.Hq + h) * D + d0;
+    if (g == 0 && d0 < a.Dv) {
+        uint16_t *outp = (uint16_t *)a.out + (q_token(a, b, i) * a.Hq + h) * a.Dv + d0;
         *(u32x2 *)outp = u32x2{pack2<DT>(acc[0] * inv, acc[1] * inv),
                                pack2<DT>(acc[2] * inv, acc[3] * inv)};
     }
@@ -149,11 +151,13 @@ hipError_t launch_t(const KernelArgs &a, hipStream_t stream) {
 
 hipError_t launch_combine(const KernelArgs &a, int dtype, hipStream_t stream) {
     if (dtype == kFp16) {
-        if (a.D == 128) return launch_t<kFp16, 128>(a, stream);
-        if (a.D == 64) return launch_t<kFp16, 64>(a, stream);
+        if (a.dv_tile == 128) return launch_t<kFp16, 128>(a, stream);
+        if (a.dv_tile == 64) return launch_t<kFp16, 64>(a, stream);
+        if (a.dv_tile == 256) return launch_t<kFp16, 256>(a, stream);
     } else {
-        if (a.D == 128) return launch_t<kBf16, 128>(a, stream);
-        if (a.D == 64) return launch_t<kBf16, 64>(a, stream);
+        if (a.dv_tile == 128) return launch_t<kBf16, 128>(a, stream);
+        if (a.dv_tile == 64) return launch_t<kBf16, 64>(a, stream);
+        if (a.dv_tile == 256) return launch_t<kBf16, 256>(a, stream);
     }
     return hipErrorInvalidValue;
 }

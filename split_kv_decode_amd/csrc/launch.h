@@ -57,7 +57,9 @@ struct KernelArgs {
     int B, Hq, Hkv, qLen, kv_cap;
     int G;                    // Hq / Hkv
     int R;                    // G * qLen rows per kv head
-    int D;
+    int D;                    // VALU kernel: head dim (= Dk = Dv)
+    int Dk, Dv;               // head dims of q / k and of v / out (multiples of 8)
+    int dv_tile;              // channels per row of ws_o (Dv rounded up to the kernel tile)
     int causal;
     int head_block, head_blocks;
     int row_block, row_blocks;
@@ -121,8 +123,37 @@ __device__ __forceinline__ size_t lse_index(const KernelArgs &a, int b, int h, i
 hipError_t launch_split_valu(const KernelArgs &a, int dtype, int layout, dim3 grid,
                              hipStream_t stream);
 
-// Matrix-core split kernel: row_block must be 64 and head_block 1.
+// Matrix-core split kernel tile widths: the head dims (Dk, Dv), multiples of
+// 8 up to 256, are padded to (64, 64), (128, 128), (192, 128) or (256, 256).
+// 16-row tiles per wave: four up to 128 x 128, two at 192 x 128, one at
+// 256 x 256 (the accumulators, Q and the K / V staging must fit one wave's
+// registers); two LDS stages per wave up to 128 x 128, else one.
+inline __host__ __device__ void mfma_tile_dims(int dk, int dv, int *tk, int *tv) {
+    if (dk <= 64 && dv <= 64) {
+        *tk = 64, *tv = 64;
+    } else if (dk <= 128 && dv <= 128) {
+        *tk = 128, *tv = 128;
+    } else if (dk <= 192 && dv <= 128) {
+        *tk = 192, *tv = 128;
+    } else {
+        *tk = 256, *tv = 256;
+    }
+}
+template <int DK, int DV>
+struct MfmaShape {
+    static constexpr int RT = (DK + DV <= 256) ? 4 : (DK + DV <= 320 ? 2 : 1);
+    static constexpr int kStages = (DK + DV <= 256) ? 2 : 1;
+};
+inline __host__ __device__ int mfma_row_block(int dk, int dv) {
+    int tk, tv;
+    mfma_tile_dims(dk, dv, &tk, &tv);
+    return (tk + tv <= 256 ? 4 : (tk + tv <= 320 ? 2 : 1)) * 16;
+}
+
+// Matrix-core split kernel: row_block = mfma_row_block(Dk, Dv), head_block 1.
 hipError_t launch_split_mfma(const KernelArgs &a, int dtype, dim3 grid, hipStream_t stream);
+hipError_t launch_split_mfma_wide(const KernelArgs &a, int dtype, dim3 grid,
+                                  hipStream_t stream);
 
 hipError_t launch_combine(const KernelArgs &a, int dtype, hipStream_t stream);
 
@@ -131,8 +162,8 @@ hipError_t launch_combine(const KernelArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_append(const KernelArgs &a, const void *k_new, const void *v_new,
                          hipStream_t stream);
 
-// Query rows per kv head from which the matrix-core path is used.
+// Query rows per kv head from which the matrix-core path is used (head dims
+// 64 or 128, Dk = Dv; every other head shape always takes it).
 constexpr int kMfmaMinRows = 32;
-constexpr int kMfmaRowBlock = 64;
 
 }  // namespace mxfa

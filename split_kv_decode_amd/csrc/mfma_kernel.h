@@ -1,0 +1,545 @@
+// Matrix-core split kernel (templates; instantiated per tile width in
+// split_mfma.hip and split_mfma_wide.hip).
+//
+// Split-KV decode attention, matrix-core path (gfx950 MFMA).
+//
+// Used when a kv head carries many query rows (R = (Hq/Hkv) * qLen >= 32, e.g.
+// GQA groups times a multi-token draft): Q K^T and P V are then dense
+// contractions with 16-row tiles, which is how the ops-transformer articles
+// place FlashAttention on a matrix unit (Q K^T and P V on the cube unit,
+// softmax and scaling on the vector unit).  fp32 accumulation throughout.
+//
+// Work decomposition.  A workgroup of 4 waves (one per SIMD, one workgroup
+// per CU) serves a segment of one stream (sequence b, kv head, block of 64
+// query rows; schedules in schedule.h).  The segment is cut into tiles of 32
+// keys and wave w takes tiles w, w + 4, w + 8, ...: every wave holds all 64
+// rows (4 row tiles of 16) and its own online-softmax state, and streams its
+// tiles with no workgroup barrier.  Two tiles per wave are in flight in
+// registers.  At the end of the segment the 4 per-wave states are merged
+// through LDS with the same log-sum-exp rule as the split merge.
+//
+// Per tile, with v_mfma_f32_16x16x32 (lane l = 16 g + p; A: row p, k-slice
+// 8g..8g+7; B: k-slice 8g..8g+7, column p; C: rows 4g..4g+3, column p):
+//   S^T = K Q^T: A = 16 keys x 32 channels of K, loaded from memory straight
+//   into the operand layout (lane (g, p) loads 16 bytes of key p), B = Q^T
+//   (the lane's query row p of each row tile, resident in registers).  Lane
+//   (g, p) receives the scores of keys 4g..4g+3 of each 16-key block for
+//   query row p, so every lane owns one query row per row tile: its running
+//   max m, running sum l and the rescale alpha are per lane (online softmax
+//   of the ops-transformer articles), the row max / sum across the 4 lane
+//   groups take two permlane swaps.
+//   O^T += V^T P^T over the 32 keys: B = P^T is the lane's own probabilities
+//   (rounded to the input type) for keys {4g..4g+3} and {16+4g..16+4g+3} --
+//   the MFMA k-slice of lane group g is taken to mean exactly these keys --
+//   and A = V^T holds the same keys for 16 channels, read from the wave's V
+//   tile in LDS with two transposed reads (ds_read_b64_tr_b16: within a
+//   16-lane group, lane 4i + c reads 4 channels of key i and lane p receives
+//   channel p of the 4 keys).  One V^T operand serves all 4 row tiles.
+// V rows are stored in LDS with their 16-byte chunks XOR-swizzled by the key
+// index, so the keys read by one transposed read hit distinct banks.
+//
+// Paged caches.  With a block table, token j of sequence b is row j % page of
+// page block_table[b][j / page].  Tiles are then aligned to multiples of 32
+// tokens and each 16-byte load instruction covers at most 8 consecutive
+// tokens, all in one page since page >= 16: the tile's pages are looked up
+// one tile ahead and read through descriptors whose range ends at the page's
+// last valid token.  Keys of the first tile that precede the segment are
+// masked.
+//
+// Head dims.  The tile widths DK x DV (64 x 64, 128 x 128, 192 x 128 or
+// 256 x 256) hold any head dims Dk <= DK, Dv <= DV that are multiples of 8:
+// the Q channels past Dk are zero, the K and V chunks past the head read a
+// valid chunk again (they meet zero Q or feed O channels that are never
+// written), and only the first Dv output channels are stored.  Wide tiles
+// keep fewer row tiles per wave (32 rows at 192 x 128, 16 at 256 x 256) and
+// one LDS stage, so registers and LDS stay within one workgroup per CU.
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+#include "schedule.h"
+
+namespace mxfa {
+namespace mfma {
+
+constexpr int kMWaves = 4;
+constexpr int kKT = 32;                           // keys per wave tile
+// how far (log2 units) a score may exceed the softmax reference before the
+// reference is moved: probabilities stay <= 2^8, exact after normalisation
+constexpr float kSlack = 8.f;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int DT>
+struct MfmaType;
+template <>
+struct MfmaType<kFp16> {
+    typedef f16x8 vec;
+    __device__ static f32x4 mma(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static _Float16 cvt(float x) { return (_Float16)x; }
+};
+template <>
+struct MfmaType<kBf16> {
+    typedef bf16x8 vec;
+    __device__ static f32x4 mma(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __bf16 cvt(float x) { return (__bf16)x; }
+};
+
+// max / sum of a per-lane value over the 4 lanes {p, p+16, p+32, p+48}
+__device__ __forceinline__ float group_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+    r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = __int_as_float(r[0]) + __int_as_float(r[1]);
+    r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+// DK / DV: the tile widths (padded head dims) of K and V; the real widths
+// a.Dk <= DK and a.Dv <= DV are multiples of 8.
+template <int DT, int DK, int DV, bool PAGED>
+struct Mfma {
+    using T = MfmaType<DT>;
+    typedef typename T::vec vec;
+    static constexpr int NCHK = DK / 8;           // 16-byte chunks per K row
+    static constexpr int NCHV = DV / 8;           // 16-byte chunks per V row
+    static constexpr int KK = DK / 32;            // k-steps of Q K^T
+    static constexpr int DB = DV / 16;            // 16-channel blocks of O
+    static constexpr int ROWK = DK * 2;           // LDS bytes per K row of one head
+    static constexpr int ROWV = DV * 2;
+    static constexpr int KTB = kKT * ROWK;        // bytes of one wave's K tile
+    static constexpr int VTB = kKT * ROWV;
+    static constexpr int LDK = kKT * NCHK / 64;   // K loads per lane per tile
+    static constexpr int LDV = kKT * NCHV / 64;   // V loads per lane per tile
+    static constexpr int RT = MfmaShape<DK, DV>::RT;          // 16-row tiles per wave
+    static constexpr int STG = MfmaShape<DK, DV>::kStages;    // LDS tile stages per wave
+    static constexpr int RB = RT * 16;            // query rows per workgroup
+    // XOR swizzle of the 16-byte chunks of a row by the key index, within
+    // aligned groups of SW chunks (a power of two)
+    static constexpr int SWK = (NCHK & (NCHK - 1)) == 0 ? NCHK : 8;
+    static constexpr int SWV = (NCHV & (NCHV - 1)) == 0 ? NCHV : 8;
+    static_assert(DK % 32 == 0 && DV % 32 == 0 && DK <= 256 && DV <= 256, "tile widths");
+    static_assert(NCHK % 8 == 0 && NCHV % 8 == 0, "loads of 4+ chunks stay in one key row group");
+
+    // LDS: during the tile loop, STG K and V tile pairs per wave; during the
+    // merge, the 4 waves' O fragments (4 sources x RT row tiles x DB x 64
+    // lanes x f32x4).
+    static constexpr int STAGE_BYTES = kMWaves * STG * (KTB + VTB);
+    static constexpr int MERGE_BYTES = kMWaves * RT * DB * 64 * 16;
+    static constexpr int BUF_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
+    struct Smem {
+        uint8_t buf[BUF_BYTES];
+        float m[kMWaves][RB];
+        float l[kMWaves][RB];
+    };
+
+    // the K and V tiles of stage `stage` of a wave, 16-byte chunks of a row
+    // XOR-swizzled by the key index
+    __device__ static uint32_t k_off(int wave, int stage, int key, int chunk) {
+        return (uint32_t)((wave * STG + stage) * (KTB + VTB) + key * ROWK +
+                          ((chunk ^ (key % SWK)) * 16));
+    }
+    __device__ static uint32_t v_off(int wave, int stage, int key, int chunk) {
+        return (uint32_t)((wave * STG + stage) * (KTB + VTB) + KTB + key * ROWV +
+                          ((chunk ^ (key % SWV)) * 16));
+    }
+    __device__ static uint32_t o_off(int src, int rt, int db, int lane) {
+        return (uint32_t)((((src * RT + rt) * DB + db) * 64 + lane) * 16);
+    }
+
+    __device__ static __forceinline__ void segment(const KernelArgs &a, Smem &sm, int b, int n, int kvh, int rb,
+                                   int t_lo, int t_hi, int slot, bool whole) {
+        b = __builtin_amdgcn_readfirstlane(b);
+        n = __builtin_amdgcn_readfirstlane(n);
+        kvh = __builtin_amdgcn_readfirstlane(kvh);
+        rb = __builtin_amdgcn_readfirstlane(rb);
+        t_lo = __builtin_amdgcn_readfirstlane(t_lo);
+        t_hi = __builtin_amdgcn_readfirstlane(t_hi);
+        slot = __builtin_amdgcn_readfirstlane(slot);
+
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int g = lane >> 4;
+        const int p = lane & 15;
+
+        // this sequence's query rows (fewer than R in a packed batch); keys
+        // past t_end are invisible to every row of the block
+        const int qn = __builtin_amdgcn_readfirstlane(q_count(a, b));
+        const int Rb = a.G * qn;
+        int t_end = t_hi;
+        if (rb * RB >= Rb) {
+            t_end = t_lo;               // a row block with no query: nothing to read
+        } else if (a.causal) {
+            const int i_max = (min(rb * RB + RB, Rb) - 1) / a.G;
+            t_end = min(t_end, i_max + n - qn + 1);
+            t_end = max(t_end, t_lo);   // an empty segment, never a negative range
+        }
+        t_end = __builtin_amdgcn_readfirstlane(t_end);
+        // first key of tile 0: a paged cache is read in page-aligned tiles
+        const int t_base = PAGED ? (t_lo & ~(kKT - 1)) : t_lo;
+        const int ntiles = t_end > t_lo ? (t_end - t_base + kKT - 1) / kKT : 0;
+        const int my_tiles = ntiles > wave ? (ntiles - wave + kMWaves - 1) / kMWaves : 0;
+
+        // the lane's query row p of each row tile, as the B operand of S^T =
+        // K Q^T; rows past R are zero and never written
+        vec qf[RT][KK];
+        int klim[RT];      // last key visible to the lane's row
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int row = rb * RB + rt * 16 + p;
+            const bool ok = row < Rb;
+            const int qi = ok ? row / a.G : 0;
+            const int qh = kvh * a.G + (ok ? row % a.G : 0);
+            klim[rt] = (a.causal && ok) ? min(t_end - 1, qi + n - qn) : t_end - 1;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                u32x4 x = {0, 0, 0, 0};
+                if (ok && 32 * kk + 8 * g < a.Dk)      // channels past the head: zero
+                    x = *(const u32x4 *)((const uint16_t *)a.q +
+                                         (q_token(a, b, qi) * a.Hq + qh) * a.Dk + 32 * kk + 8 * g);
+                qf[rt][kk] = __builtin_bit_cast(vec, x);
+            }
+        }
+
+        // K/V of sequence b; the descriptor range ends with token t_end - 1,
+        // so loads past it return zeros without touching memory
+        const uint32_t ktok = (uint32_t)a.Hkv * a.Dk * 2;   // bytes per token row
+        const uint32_t vtok = (uint32_t)a.Hkv * a.Dv * 2;
+        const size_t kv0 = kv_token0(a, b);
+        const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(
+            (const uint16_t *)a.k + (PAGED ? 0 : kv0 * a.Hkv * a.Dk), (uint32_t)t_end * ktok);
+        const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(
+            (const uint16_t *)a.v + (PAGED ? 0 : kv0 * a.Hkv * a.Dv), (uint32_t)t_end * vtok);
+        // K and V row-major: load instruction u of a tile covers the flat
+        // chunks 64 u .. 64 u + 63 of the tile's rows, lane l chunk
+        // (64 u + l) % NCH of key (64 u + l) / NCH.  The lane's byte offset
+        // from the first key of its instruction (kfirst(u) = 64 u / NCH);
+        // chunks past the head's width read chunk 0 again (their Q channels
+        // are zero and their O channels are never written).
+        uint32_t koff[LDK], voff[LDV];
+#pragma unroll
+        for (int u = 0; u < LDK; ++u) {
+            const int f = 64 * u + lane, key = f / NCHK, ch = f % NCHK;
+            koff[u] = (uint32_t)(key - 64 * u / NCHK) * ktok + (uint32_t)kvh * a.Dk * 2 +
+                      16u * (8 * ch < a.Dk ? ch : 0);
+        }
+#pragma unroll
+        for (int u = 0; u < LDV; ++u) {
+            const int f = 64 * u + lane, key = f / NCHV, ch = f % NCHV;
+            voff[u] = (uint32_t)(key - 64 * u / NCHV) * vtok + (uint32_t)kvh * a.Dv * 2 +
+                      16u * (8 * ch < a.Dv ? ch : 0);
+        }
+
+        u32x4 ks[LDK], vs[LDV];
+        // tile index of the wave's i-th tile; indices past the segment are
+        // clamped to ntiles, whose keys all lie past t_end (loads read nothing)
+        auto tile_of = [&](int i) { return min(wave + kMWaves * i, ntiles); };
+        // paged: a tile (32 keys, aligned) lies in one page, or in two when the
+        // page is 16 tokens; its block-table entries are read with vector
+        // loads one tile ahead (tracked with the K/V loads, no scalar-cache
+        // wait in the loop) through a descriptor that ends at the last page
+        // holding a token below t_end (entries past it read as 0 and are not
+        // used).  pg_cur: the pages of the tile loaded next.  The keys of one
+        // load instruction (at most 8 consecutive, NCH a multiple of 8) never
+        // straddle a page boundary.
+        const int page = 1 << a.log_page;
+        const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(
+            PAGED ? (const void *)(a.block_table + (size_t)b * a.max_pages) : nullptr,
+            PAGED ? (uint32_t)((t_end + page - 1) >> a.log_page) * 4u : 0u);
+        uint32_t pg_cur[2] = {0u, 0u};
+        auto fetch_pages = [&](int j, uint32_t (&pg)[2]) {
+            const int t0 = t_base + j * kKT;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                pg[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                    bt_rsrc, (uint32_t)((t0 + 16 * h) >> a.log_page) * 4u, 0, 0);
+        };
+        // the load whose first key is tok, from page entry e, through a
+        // descriptor whose range ends at the last token below t_end
+        auto page_load = [&](const void *pool, uint32_t tokb, size_t row_elems, int tok,
+                             uint32_t e, uint32_t lane_off) {
+            const int pi = tok >> a.log_page;
+            const int valid = t_end - (pi << a.log_page);
+            const int pg = clampi(__builtin_amdgcn_readfirstlane((int)e), 0, a.num_pages - 1);
+            const uint32_t rng = valid <= 0 ? 0u : (uint32_t)min(valid, page) * tokb;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(
+                (const uint16_t *)pool + ((size_t)pg << a.log_page) * row_elems, rng);
+            return load16(r, (uint32_t)(tok & (page - 1)) * tokb + lane_off);
+        };
+        auto gload_v = [&](int j) {
+            const int t0 = PAGED ? t_base + j * kKT : t_lo + j * kKT;
+#pragma unroll
+            for (int u = 0; u < LDV; ++u) {
+                const int tok = t0 + 64 * u / NCHV;
+                if constexpr (PAGED)
+                    vs[u] = page_load(a.v, vtok, (size_t)a.Hkv * a.Dv, tok, pg_cur[tok - t0 >= 16],
+                                      voff[u]);
+                else
+                    vs[u] = load16(vrsrc, (uint32_t)tok * vtok + voff[u]);
+            }
+        };
+        auto gload_k = [&](int j) {
+            const int t0 = PAGED ? t_base + j * kKT : t_lo + j * kKT;
+#pragma unroll
+            for (int u = 0; u < LDK; ++u) {
+                const int tok = t0 + 64 * u / NCHK;
+                if constexpr (PAGED)
+                    ks[u] = page_load(a.k, ktok, (size_t)a.Hkv * a.Dk, tok, pg_cur[tok - t0 >= 16],
+                                      koff[u]);
+                else
+                    ks[u] = load16(krsrc, (uint32_t)tok * ktok + koff[u]);
+            }
+        };
+
+        // online softmax with a lazily moved reference: every lane keeps the
+        // reference m of its row (the same in the row's 4 lanes) and a partial
+        // sum l over its own keys; probabilities are exp2(x - m) <= 2^kSlack,
+        // and m (with O and l) moves only when a score passes m + kSlack
+        float m_run[RT], l_run[RT];
+        f32x4 o[RT][DB];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            m_run[rt] = kNegInf;
+            l_run[rt] = 0.f;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+        auto compute = [&](int set, int j, int jn, int jnn) {
+            const int key0 = t_base + j * kKT;
+            // paged: keys of the first tile before t_lo are not part of the segment
+            const int vis_lo = (PAGED && key0 < t_lo) ? t_lo - key0 - 4 * g : INT32_MIN;
+            // stage this tile's K and V rows in the wave's LDS buffer `set`
+#pragma unroll
+            for (int u = 0; u < LDK; ++u)
+                *(u32x4 *)(sm.buf + k_off(wave, set, (64 * u + lane) / NCHK, (64 * u + lane) % NCHK)) =
+                    ks[u];
+            gload_k(jn);       // the next tile streams while this one is computed
+            uint32_t pg_nxt[2];
+            if constexpr (PAGED) fetch_pages(jnn, pg_nxt);
+#pragma unroll
+            for (int u = 0; u < LDV; ++u)
+                *(u32x4 *)(sm.buf + v_off(wave, set, (64 * u + lane) / NCHV, (64 * u + lane) % NCHV)) =
+                    vs[u];
+            gload_v(jn);
+            if constexpr (PAGED) {
+                pg_cur[0] = pg_nxt[0];
+                pg_cur[1] = pg_nxt[1];
+            }
+            wave_lds_sync();   // the tiles written above are visible to the whole wave
+            // S^T for 4 row tiles x 2 blocks of 16 keys, in log2 units; the A
+            // operand (16 keys x 32 channels of K) serves all row tiles
+            vec ka[2][KK];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    ka[kb][kk] = __builtin_bit_cast(
+                        vec, *(const u32x4 *)(sm.buf + k_off(wave, set, 16 * kb + p, 4 * kk + g)));
+            float x[RT][2][4];
+            float mloc[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                // key 16 kb + 4 g + i of the tile is visible iff 16 kb + i <= vis
+                const int vis = klim[rt] - key0 - 4 * g;
+                mloc[rt] = kNegInf;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        acc = T::mma(ka[kb][kk], qf[rt][kk], acc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = (16 * kb + i <= vis && 16 * kb + i >= vis_lo)
+                                            ? acc[i] * a.qscale : kNegInf;
+                        x[rt][kb][i] = v;
+                        mloc[rt] = fmaxf(mloc[rt], v);
+                    }
+                }
+            }
+            // move the reference where a score passed it by more than kSlack
+            bool move = false;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) move |= mloc[rt] > m_run[rt] + kSlack;
+            if (__builtin_amdgcn_readfirstlane(__any(move) ? 1 : 0)) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const float m_new = fmaxf(m_run[rt], group_max(mloc[rt]));
+                    const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run[rt] - m_new);
+                    m_run[rt] = m_new;
+                    l_run[rt] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) o[rt][db] *= alpha;
+                }
+            }
+            vec pb[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float m_use = m_run[rt] == kNegInf ? 0.f : m_run[rt];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = fast_exp2(x[rt][kb][i] - m_use);
+                        l_run[rt] += e;
+                        pb[rt][4 * kb + i] = T::cvt(e);
+                    }
+            }
+            // O^T += V^T P^T; the V^T operand of a channel block serves all row tiles
+            const int kr = 4 * g + (p >> 2);            // key read by this lane
+            const int c = p & 3;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int chunk = 2 * db + (c >> 1);
+                const uint32_t half = 8u * (c & 1);
+                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(sm.buf + v_off(wave, set, kr, chunk) + half));
+                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(sm.buf + v_off(wave, set, kr + 16, chunk) + half));
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const s16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    o[rt][db] = T::mma(__builtin_bit_cast(vec, va), pb[rt], o[rt][db]);
+            }
+        };
+        // one tile in flight per wave: the next tile's loads are issued as
+        // soon as this tile is in LDS
+        if constexpr (PAGED) fetch_pages(tile_of(0), pg_cur);
+        gload_v(tile_of(0));
+        gload_k(tile_of(0));
+        if constexpr (PAGED) fetch_pages(tile_of(1), pg_cur);
+        for (int i = 0; i < my_tiles; ++i) {
+            const int j = tile_of(i);
+            compute(STG == 2 ? (i & 1) : 0, j, tile_of(i + 1), tile_of(i + 2));
+        }
+
+        // the row sums over the 4 lanes of each row
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) l_run[rt] = group_sum(l_run[rt]);
+
+        // merge the 4 waves' states: the waves split the RT row tiles and
+        // their DB channel blocks between them (WPR waves per row tile, wave
+        // w takes row tile w % RT and the channel blocks w / RT + k * WPR)
+        __syncthreads();                       // every wave is done with its V tiles
+        if (g == 0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                sm.m[wave][rt * 16 + p] = m_run[rt];
+                sm.l[wave][rt * 16 + p] = l_run[rt];
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) *(f32x4 *)(sm.buf + o_off(wave, rt, db, lane)) = o[rt][db];
+        __syncthreads();
+        constexpr int WPR = kMWaves / RT;      // waves per row tile
+        constexpr int NDB = DB / WPR;          // channel blocks per wave
+        static_assert(kMWaves % RT == 0 && DB % WPR == 0, "merge split");
+        const int mrt = wave % RT;             // row tile this wave finishes
+        const int part = wave / RT;            // its share of the channel blocks
+        const int rloc = mrt * 16 + p;
+        float msrc[kMWaves];
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kMWaves; ++w) {
+            msrc[w] = sm.m[w][rloc];
+            M = fmaxf(M, msrc[w]);
+        }
+        float L = 0.f;
+        f32x4 acc[NDB];
+#pragma unroll
+        for (int k = 0; k < NDB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kMWaves; ++w) {
+            const float sc = msrc[w] == kNegInf ? 0.f : fast_exp2(msrc[w] - M);
+            L += sc * sm.l[w][rloc];
+#pragma unroll
+            for (int k = 0; k < NDB; ++k)
+                acc[k] += sc * *(const f32x4 *)(sm.buf + o_off(w, mrt, part + k * WPR, lane));
+        }
+
+        // epilogue: the lane's row, channels 16 db + 4 g .. + 3 of its blocks
+        const int row = rb * RB + rloc;
+        if (row < Rb) {
+            const int qi = row / a.G;
+            const int qh = kvh * a.G + row % a.G;
+            const bool empty = !(L > 0.f);
+            const float inv = empty ? 0.f : 1.f / L;
+            const float lse2 = empty ? kNegInf : M + fast_log2(L);
+            if (whole) {
+                uint16_t *op = (uint16_t *)a.out + (q_token(a, b, qi) * a.Hq + qh) * a.Dv;
+#pragma unroll
+                for (int k = 0; k < NDB; ++k) {
+                    const int c0 = 16 * (part + k * WPR) + 4 * g;
+                    if (c0 < a.Dv)                 // channels past the head: not written
+                        *(u32x2 *)(op + c0) = u32x2{pack2<DT>(acc[k][0] * inv, acc[k][1] * inv),
+                                                    pack2<DT>(acc[k][2] * inv, acc[k][3] * inv)};
+                }
+                if (part == 0 && g == 0 && a.lse)
+                    a.lse[lse_index(a, b, qh, qi)] = empty ? kNegInf : lse2 * kLn2;
+            } else {
+                const size_t e = (size_t)slot * RB + rloc;   // head_block = 1
+#pragma unroll
+                for (int k = 0; k < NDB; ++k)
+                    *(f32x4 *)(a.ws_o + e * DV + 16 * (part + k * WPR) + 4 * g) = acc[k] * inv;
+                if (part == 0 && g == 0) a.ws_lse[e] = lse2;
+            }
+        }
+        __syncthreads();                       // the next segment reuses the LDS
+    }
+};
+
+// One workgroup per CU, one wave per SIMD: each wave keeps the block's rows
+// of accumulators and one K/V tile in registers.
+
+template <int DT, int DK, int DV, int SCHED, bool PAGED>
+__global__ __launch_bounds__(kMWaves * 64)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+void split_kv_mfma_kernel(KernelArgs a) {
+    using M = Mfma<DT, DK, DV, PAGED>;
+    __shared__ __attribute__((aligned(16))) typename M::Smem sm;
+    drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
+                                 bool whole) {
+        M::segment(a, sm, b, n, hb, rb, t_lo, t_hi, slot, whole);
+    });
+}
+
+template <int DT, int DK, int DV>
+hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
+    if (a.row_block != Mfma<DT, DK, DV, false>::RB || a.head_block != 1 || a.Dk > DK ||
+        a.Dv > DV)
+        return hipErrorInvalidValue;
+    KernelArgs args = a;
+    void *kargs[] = {&args};
+    const bool paged = a.block_table != nullptr;
+    const void *fn =
+        a.schedule == kBalanced
+            ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, kBalanced, true>
+                     : (const void *)&split_kv_mfma_kernel<DT, DK, DV, kBalanced, false>)
+            : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, kFixed, true>
+                     : (const void *)&split_kv_mfma_kernel<DT, DK, DV, kFixed, false>);
+    return hipLaunchKernel(fn, grid, dim3(kMWaves * 64), kargs, 0, stream);
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const KernelArgs &a, int dtype, dim3 grid, hipStream_t stream) {
+    return dtype == kFp16 ? launch_t<kFp16, DK, DV>(a, grid, stream)
+                          : launch_t<kBf16, DK, DV>(a, grid, stream);
+}
+
+}  // namespace mfma
+}  // namespace mxfa

@@ -22,6 +22,7 @@ PATH_NAMES = {0: "valu", 1: "mfma"}
 EXPORTS = ("mxfa_fwd_kvcache", "mxfa_fwd_kvcache_ws", "mxfa_workspace_size",
            "mxfa_fwd_kvcache_paged", "mxfa_fwd_kvcache_paged_ws", "mxfa_workspace_size_paged",
            "mxfa_fwd_kvcache_append", "mxfa_fwd_kvcache_paged_append", "mxfa_fwd_varlen",
+           "mxfa_fwd_kvcache_dkdv", "mxfa_workspace_size_dkdv",
            "mxfa_plan", "mxfa_last_plan", "mxfa_set_timing_events",
            "mxfa_status_string", "mxfa_version")
 
@@ -80,6 +81,10 @@ def lib() -> ctypes.CDLL:
     L.mxfa_fwd_kvcache_paged_append.restype = ci
     L.mxfa_fwd_varlen.argtypes = [vp] * 7 + [ci] * 11 + [vp, sz, vp]
     L.mxfa_fwd_varlen.restype = ci
+    L.mxfa_fwd_kvcache_dkdv.argtypes = [vp] * 6 + [ci] * 10 + [vp, sz, vp]
+    L.mxfa_fwd_kvcache_dkdv.restype = ci
+    L.mxfa_workspace_size_dkdv.argtypes = [ci] * 10 + [ctypes.POINTER(sz)]
+    L.mxfa_workspace_size_dkdv.restype = ci
     L.mxfa_plan.argtypes = [ci] * 10 + [ctypes.POINTER(Plan)]
     L.mxfa_plan.restype = ci
     L.mxfa_last_plan.argtypes = [ctypes.POINTER(Plan)]
@@ -405,3 +410,64 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqle
     if st != MXFA_OK:
         raise MxfaError(st, "mxfa_fwd_varlen")
     return out, lse
+
+
+def fwd_kvcache_dkdv(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
+                     out=None, lse=None, return_lse: bool = True, num_splits: int = 0,
+                     workspace=None, stream=None) -> Tuple[object, Optional[object]]:
+    """Decode attention with different key and value head dims: q [B, qLen,
+    Hq, Dk], k_cache [B, kv_cap, Hkv, Dk], v_cache [B, kv_cap, Hkv, Dv];
+    returns out [B, qLen, Hq, Dv] and lse [B, Hq, qLen]."""
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, qLen, Hq, Dk = q.shape
+    Bk, kv_cap, Hkv, Dk2 = k_cache.shape
+    Dv = v_cache.shape[3]
+    if Bk != B or Dk2 != Dk or tuple(v_cache.shape[:3]) != (B, kv_cap, Hkv):
+        raise ValueError("k_cache [B, kv_cap, Hkv, Dk] and v_cache [B, kv_cap, Hkv, Dv] must "
+                         "match q")
+    dt = _dtype_code(q)
+    if cache_seqlens is not None:
+        if (cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda
+                or tuple(cache_seqlens.shape) != (B,) or not cache_seqlens.is_contiguous()):
+            raise ValueError("cache_seqlens must be a contiguous int32 GPU tensor of shape [B]")
+    if out is None:
+        out = torch.empty((B, qLen, Hq, Dv), dtype=q.dtype, device=q.device)
+    elif (tuple(out.shape) != (B, qLen, Hq, Dv) or out.dtype != q.dtype
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor [B, qLen, Hq, Dv] of q's dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, qLen), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, qLen)
+                              or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, qLen]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib().mxfa_fwd_kvcache_dkdv(ptr(q), ptr(k_cache), ptr(v_cache), ptr(cache_seqlens),
+                                         ptr(out), ptr(lse), B, Hq, Hkv, Dk, Dv, qLen, kv_cap,
+                                         int(bool(causal)), dt, int(num_splits), ptr(workspace),
+                                         wsb, ctypes.c_void_p(stream))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_fwd_kvcache_dkdv")
+    return out, lse
+
+
+def workspace_size_dkdv(B, Hq, Hkv, Dk, Dv, qLen, kv_cap, causal=False, dtype=MXFA_FP16,
+                        num_splits=0) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().mxfa_workspace_size_dkdv(B, Hq, Hkv, Dk, Dv, qLen, kv_cap, int(causal),
+                                        int(dtype), int(num_splits), ctypes.byref(n))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_workspace_size_dkdv")
+    return n.value

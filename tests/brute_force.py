@@ -21,8 +21,9 @@ def attention(q_bits, k_bits, v_bits, seqlens, causal, dtype):
     v = decode(v_bits, dtype)
     B, qLen, Hq, D = q.shape
     _, cap, Hkv, _ = k.shape
+    Dv = v.shape[3]                                    # may differ from D (= Dk)
     G = Hq // Hkv
-    out = np.zeros((B, qLen, Hq, D))
+    out = np.zeros((B, qLen, Hq, Dv))
     lse = np.full((B, Hq, qLen), -np.inf)
     for b in range(B):
         n = cap if seqlens is None else int(np.clip(seqlens[b], 0, cap))

@@ -132,6 +132,43 @@ def pin_torch_sdpa_fp64(lib_path):
         assert np.allclose(l1, lref, rtol=0, atol=1e-12)
 
 
+def pin_separate_key_and_value_dims(lib_path):
+    """Dk != Dv (the MLA heads of the SmallQ README's support range): the
+    brute force and torch SDPA in float64 (which also takes a V of another
+    width, scale 1/sqrt(Dk)), and the value-slicing identity: each output
+    channel depends on its V channel alone, so a V of Dv channels gives the
+    first Dv channels of the output for a wider V."""
+    import torch.nn.functional as F
+    g = torch.Generator().manual_seed(13)
+    for (B, qLen, Hq, Hkv, Dk, Dv, cap, lens, causal, dt) in [
+            (2, 3, 4, 2, 24, 16, 9, [9, 4], True, "bf16"),
+            (1, 2, 2, 1, 16, 40, 7, None, False, "fp16"),
+            (1, 4, 8, 2, 192, 128, 30, [30], True, "bf16")]:
+        q = _rand((B, qLen, Hq, Dk), dt, g)
+        k = _rand((B, cap, Hkv, Dk), dt, g)
+        v = _rand((B, cap, Hkv, Dv), dt, g)
+        sl = None if lens is None else np.array(lens, np.int32)
+        o1, l1 = oracle.attention(q, k, v, sl, causal, dt, lib_path=lib_path)
+        assert o1.shape == (B, qLen, Hq, Dv)
+        o2, l2 = brute_force.attention(_bits(q), _bits(k), _bits(v), sl, causal, dt)
+        assert np.allclose(o1, o2, rtol=0, atol=1e-12)
+        assert np.array_equal(l1, l2) or np.allclose(l1, l2, rtol=0, atol=1e-12)
+        if sl is None:
+            qt = q.to(torch.float64).permute(0, 2, 1, 3)
+            kt = k.to(torch.float64).permute(0, 2, 1, 3)
+            vt = v.to(torch.float64).permute(0, 2, 1, 3)
+            ii = torch.arange(qLen)[:, None]
+            jj = torch.arange(cap)[None, :]
+            mask = (jj <= ii + cap - qLen) if causal else torch.ones(qLen, cap, dtype=torch.bool)
+            ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                                 enable_gqa=True).permute(0, 2, 1, 3)
+            assert np.allclose(o1, ref.numpy(), rtol=0, atol=1e-12)
+        # slicing V to its first 8 channels slices the output, lse unchanged
+        o3, l3 = oracle.attention(q, k, v[..., :8].contiguous(), sl, causal, dt,
+                                  lib_path=lib_path)
+        assert np.array_equal(o3, o1[..., :8]) and np.array_equal(l3, l1)
+
+
 # --------------------------------------------------------------------------
 # closed forms
 
@@ -382,6 +419,7 @@ ALL_PINS = [
     pin_bf16_decode_exhaustive,
     pin_brute_force_tiny,
     pin_torch_sdpa_fp64,
+    pin_separate_key_and_value_dims,
     pin_single_key,
     pin_identical_keys,
     pin_dominant_key,

@@ -109,7 +109,7 @@ INV, UNS = mxfa.MXFA_ERR_INVALID_ARG, mxfa.MXFA_ERR_UNSUPPORTED
     (dict(Hkv=0), INV), (dict(D=0), INV), (dict(Hq=6, Hkv=4), INV),
     (dict(causal=2), INV), (dict(causal=-1), INV), (dict(dtype=2), INV), (dict(dtype=-1), INV),
     (dict(B=2**30, cap=2**30), INV),                       # byte size overflow
-    (dict(D=96), UNS), (dict(D=256), UNS), (dict(D=32), UNS), (dict(B=70000), UNS),
+    (dict(D=100), UNS), (dict(D=264), UNS), (dict(D=4), UNS), (dict(B=70000), UNS),
     (dict(cap=2**16, Hq=128, Hkv=128), UNS),               # cache past 2^30 bytes per sequence
     (dict(cap=1, Hq=8192, Hkv=8192), UNS),                 # 1024-token slack past 2^30 bytes
 ])
@@ -141,7 +141,7 @@ def _call_paged(ws_entry=False, num_splits=0, **kw):
     (dict(page=1 << 17, Hq=64, Hkv=64), UNS),              # one page past 2^30 bytes
     (dict(page=1 << 20, max_pages=1 << 12), UNS),          # logical capacity past INT_MAX
     (dict(num_pages=1 << 40 >> 20, page=1 << 20, Hq=64, Hkv=64, max_pages=1), UNS),
-    (dict(D=96), UNS), (dict(Hq=6, Hkv=4), INV), (dict(causal=3), INV), (dict(dtype=5), INV),
+    (dict(D=100), UNS), (dict(Hq=6, Hkv=4), INV), (dict(causal=3), INV), (dict(dtype=5), INV),
 ])
 def test_paged_arguments_rejected_before_any_hip_call(kw, status):
     assert _call_paged(**kw) == status
@@ -183,7 +183,7 @@ def _call_append(paged=False, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(new_len=-1), INV), (dict(sl=0), INV), (dict(sl=0x90002), INV),
     (dict(kn=0), INV), (dict(vn=0), INV), (dict(kn=0x70008), INV),
-    (dict(k=0), INV), (dict(num_splits=-2), INV), (dict(D=80), UNS),
+    (dict(k=0), INV), (dict(num_splits=-2), INV), (dict(D=84), UNS),
     (dict(qLen=0, k=0), INV),                    # the cache is still written
     (dict(new_len=2 ** 30, B=2 ** 15, Hkv=1024, Hq=1024), INV),   # k_new byte size
 ])
@@ -216,7 +216,7 @@ def _call_varlen(**kw):
     (dict(cq=0), INV), (dict(ck=0), INV), (dict(cq=0x90002), INV), (dict(q=0), INV),
     (dict(k=0), INV), (dict(out=0x40004), INV), (dict(total_q=-1), INV),
     (dict(total_k=-1), INV), (dict(max_q=-1), INV), (dict(max_k=-1), INV),
-    (dict(num_splits=-1), INV), (dict(D=32), UNS), (dict(Hq=3), INV),
+    (dict(num_splits=-1), INV), (dict(D=36), UNS), (dict(Hq=3), INV),
     (dict(max_k=1 << 22, Hkv=128, Hq=128), UNS),           # one sequence past 2^30 bytes
 ])
 def test_varlen_arguments_rejected_before_any_hip_call(kw, status):
@@ -227,6 +227,38 @@ def test_varlen_empty_problems():
     assert _call_varlen(B=0) == mxfa.MXFA_OK
     assert _call_varlen(total_q=0, q=0, out=0) == mxfa.MXFA_OK
     assert _call_varlen(max_q=0) == mxfa.MXFA_OK
+
+
+def _call_dkdv(**kw):
+    a = dict(q=0x10000, k=0x20000, v=0x30000, sl=0, out=0x40000, lse=0x50000, B=2, Hq=8,
+             Hkv=2, Dk=192, Dv=128, qLen=1, cap=64, causal=0, dtype=1, num_splits=0)
+    a.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    return m.lib().mxfa_fwd_kvcache_dkdv(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["sl"]),
+                                         vp(a["out"]), vp(a["lse"]), a["B"], a["Hq"], a["Hkv"],
+                                         a["Dk"], a["Dv"], a["qLen"], a["cap"], a["causal"],
+                                         a["dtype"], a["num_splits"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Dk=0), INV), (dict(Dv=-8), INV), (dict(Dk=100), UNS), (dict(Dv=264), UNS),
+    (dict(Dk=4), UNS), (dict(q=0), INV), (dict(v=0x30008), INV), (dict(num_splits=-1), INV),
+    (dict(cap=1 << 20, Hkv=8, Hq=8, Dk=256), UNS),         # a sequence past 2^30 bytes
+])
+def test_dkdv_arguments_rejected_before_any_hip_call(kw, status):
+    assert _call_dkdv(**kw) == status
+
+
+def test_plan_routes_head_dims():
+    # 64 / 128 keep the VALU path for few rows; every other head shape takes
+    # the matrix-core kernel with its padded tiles (fewer rows per block when wide)
+    assert m.plan(4, 32, 8, 128, 1, 4096, 0, 1).path == 0
+    for D, rb in ((96, 64), (32, 64), (256, 16), (8, 64), (160, 16)):
+        p = m.plan(4, 32, 8, D, 1, 4096, 0, 1)
+        assert p.path == 1 and p.row_block == rb, D
+    n = ctypes.c_size_t()
+    assert m.lib().mxfa_workspace_size_dkdv(2, 8, 2, 192, 128, 1, 64, 0, 0, -1,
+                                            ctypes.byref(n)) == INV
 
 
 def test_empty_problem_is_a_no_op():
@@ -246,7 +278,7 @@ def test_workspace_size_argument_checks():
     L = m.lib()
     assert L.mxfa_workspace_size(1, 8, 2, 128, 1, 64, 0, 0, 0, None) == INV
     assert L.mxfa_workspace_size(1, 8, 3, 128, 1, 64, 0, 0, 0, ctypes.byref(n)) == INV
-    assert L.mxfa_workspace_size(1, 8, 2, 80, 1, 64, 0, 0, 0, ctypes.byref(n)) == UNS
+    assert L.mxfa_workspace_size(1, 8, 2, 84, 1, 64, 0, 0, 0, ctypes.byref(n)) == UNS
     assert L.mxfa_workspace_size(1, 8, 2, 128, 1, 64, 0, 0, -3, ctypes.byref(n)) == INV
 
 

@@ -356,3 +356,21 @@ def varlen_bytes(w: VarlenWorkload) -> int:
     tq, tk = sum(w.qlens), sum(w.klens)
     return (2 * tq * w.Hq * w.D * 2 + 2 * tk * w.Hkv * w.D * 2 + tq * w.Hq * 4
             + 2 * (w.B + 1) * 4)
+
+
+def make_inputs_dkdv(B: int, qLen: int, Hq: int, Hkv: int, Dk: int, Dv: int, kv_cap: int,
+                     lengths: List[int], dtype: str, sigma: float, seed: int):
+    """Inputs with different key and value head dims, drawn like make_inputs
+    (q, then K and V rows per sequence, N(0, sigma^2) rounded to the dtype;
+    cache rows at or past a length are NaN): q [B, qLen, Hq, Dk],
+    k [B, kv_cap, Hkv, Dk], v [B, kv_cap, Hkv, Dv], cache_seqlens int32 [B]."""
+    g = torch.Generator().manual_seed(seed)
+    td = torch.float16 if dtype == "fp16" else torch.bfloat16
+    q = (torch.randn(B, qLen, Hq, Dk, generator=g) * sigma).to(td)
+    k = torch.full((B, kv_cap, Hkv, Dk), float("nan"), dtype=td)
+    v = torch.full((B, kv_cap, Hkv, Dv), float("nan"), dtype=td)
+    for b in range(B):
+        n = max(0, min(lengths[b], kv_cap))
+        k[b, :n] = (torch.randn(n, Hkv, Dk, generator=g) * sigma).to(td)
+        v[b, :n] = (torch.randn(n, Hkv, Dv, generator=g) * sigma).to(td)
+    return q, k, v, torch.tensor(lengths, dtype=torch.int32)
