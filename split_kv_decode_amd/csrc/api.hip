@@ -207,8 +207,10 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     if ((long long)head_blocks * row_blocks > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
     pl.num_cus = num_cus;
     const long long streams = (long long)p.B * head_blocks * row_blocks;
+    // the partial-result floor counts the rows a block actually holds
+    const int rows_held = (int)(R < pl.row_block ? R : pl.row_block);
     const int min_chunk =
-        ceil_div(16 * pl.row_block > 64 ? 16 * pl.row_block : 64, kChunkAlign) * kChunkAlign;
+        ceil_div(16 * rows_held > 64 ? 16 * rows_held : 64, kChunkAlign) * kChunkAlign;
 
     int S, chunk;
     if (p.kv_cap == 0) {

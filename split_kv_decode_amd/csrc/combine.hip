@@ -16,10 +16,11 @@
 // workgroups whose share of the concatenated streams overlaps it.  A stream
 // served by one workgroup was written directly by the split kernel and is
 // skipped; a stream with no token at all gets O = 0, lse = -inf here.  The
-// weights are computed
-// with one partition per lane and kept in LDS; the weighted sum then splits
-// the wave into NG groups of D/4 lanes (4 channels per lane, 16-byte loads),
-// each group taking every NG-th partition with UNR loads in flight, and the
+// wave splits into NG groups of D/4 lanes (4 channels per lane, 16-byte
+// loads), each group taking every NG-th partition; the partitions' lse values
+// (one per lane) and the first 16 partition rows per lane are loaded
+// together, so the maximum and the weights cost no extra memory round trip.
+// A partition's weight travels from its lane by a cross-lane read, and the
 // groups are summed with cross-lane exchanges.  D here is the channel count
 // of a partial row (the head dim, or the matrix-core kernel's padded V tile);
 // only the first Dv channels are written out.
@@ -29,19 +30,24 @@
 namespace mxfa {
 namespace {
 
-constexpr int kRowsPerBlock = 4;
-constexpr int kMaxStaged = 256;     // weights staged in LDS per pass
+constexpr int kWaves = 4;                    // waves per workgroup
 
-template <int DT, int D>
-__global__ __launch_bounds__(kRowsPerBlock * 64) void combine_kernel(KernelArgs a) {
+// WPR waves per output row: 1 when rows have few partials, 4 (one workgroup
+// per row) when they have many, so that the partial rows of one output row
+// are read by 4 waves at once.
+template <int DT, int D, int WPR>
+__global__ __launch_bounds__(kWaves * 64) void combine_kernel(KernelArgs a) {
     constexpr int LPG = D / 4;                  // lanes per group
-    constexpr int NG = 64 / LPG;                // groups per wave (2 or 4)
-    constexpr int UNR = 4;
-    __shared__ float lds_w[kRowsPerBlock][kMaxStaged];
+    constexpr int NG = 64 / LPG;                // groups per wave (1, 2 or 4)
+    constexpr int UNR = WPR == 1 ? 16 : 8;      // partial rows in flight per lane
+    constexpr int RPB = kWaves / WPR;           // rows per workgroup
+    constexpr int STEP = WPR * NG;              // partials between a lane's loads
+    __shared__ f32x4 lds_acc[WPR > 1 ? WPR : 1][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const long long row = (long long)blockIdx.x * kRowsPerBlock + wave;
+    const int sub = wave % WPR;                 // this wave's share of the partials
+    const long long row = (long long)blockIdx.x * RPB + wave / WPR;
     const long long nrows = (long long)a.B * a.Hq * a.qLen;
     if (row >= nrows) return;                   // whole wave exits together
     const int i = (int)(row % a.qLen);
@@ -79,57 +85,80 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void combine_kernel(KernelArgs 
     const size_t e0 = ((size_t)first * a.head_block + hx) * a.row_block + r;
     const float *lrow = a.ws_lse + e0;           // entry of slot k at lrow[k * stride]
     const float *orow = a.ws_o + e0 * D;         // row of slot k at orow[k * stride * D]
-
-    float M = kNegInf;
-    for (int s = lane; s < count; s += 64) M = fmaxf(M, lrow[(size_t)s * stride]);
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
-
-    const int g = lane / LPG;
+    const int g = sub * NG + lane / LPG;        // first partial of this lane
     const int d0 = (lane % LPG) * 4;
+    auto orow_of = [&](int s) { return *(const f32x4 *)(orow + (size_t)s * stride * D + d0); };
+
+    // the partials' lse (lane s holds partial s < 64) and the first UNR * STEP
+    // partial rows are loaded together, before the maximum is known
+    const float lv = lane < count ? lrow[(size_t)lane * stride] : kNegInf;
+    f32x4 x[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+        const int sp = g + u * STEP;
+        x[u] = sp < count ? orow_of(sp) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float M = lv;
+    for (int sp = lane + 64; sp < count; sp += 64) M = fmaxf(M, lrow[(size_t)sp * stride]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     if (M != kNegInf) {
-        for (int s0 = 0; s0 < count; s0 += kMaxStaged) {
-            const int cnt = min(count - s0, kMaxStaged);
-            for (int s = lane; s < cnt; s += 64) {
-                const float w = fast_exp2(lrow[(size_t)(s0 + s) * stride] - M);
-                lds_w[wave][s] = w;                     // -inf partials weigh 0
-                L += w;
+        // weight of partial s < 64 sits in lane s; -inf partials weigh 0
+        const float wl = fast_exp2(lv - M);
+        L = wl;
+        for (int sp = lane + 64; sp < count; sp += 64) L += fast_exp2(lrow[(size_t)sp * stride] - M);
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int sp = g + u * STEP;
+            const float w = __shfl(wl, sp & 63);
+            if (sp < count)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, x[u][j], acc[j]);
+        }
+        // more partials than the first batch holds
+        for (int s0 = UNR * STEP; s0 < count; s0 += UNR * STEP) {
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int sp = s0 + g + u * STEP;
+                x[u] = sp < count ? orow_of(sp) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            wave_lds_sync();
-            int s = g;
-            for (; s + (UNR - 1) * NG < cnt; s += UNR * NG) {
-                f32x4 x[UNR];
 #pragma unroll
-                for (int u = 0; u < UNR; ++u)
-                    x[u] = *(const f32x4 *)(orow + (size_t)(s0 + s + u * NG) * stride * D + d0);
-#pragma unroll
-                for (int u = 0; u < UNR; ++u) {
-                    const float w = lds_w[wave][s + u * NG];
+            for (int u = 0; u < UNR; ++u) {
+                const int sp = s0 + g + u * STEP;
+                const float ws = __shfl(wl, sp & 63);      // every lane takes part
+                if (sp < count) {
+                    const float w = sp < 64 ? ws : fast_exp2(lrow[(size_t)sp * stride] - M);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, x[u][j], acc[j]);
                 }
             }
-            for (; s < cnt; s += NG) {
-                const f32x4 x = *(const f32x4 *)(orow + (size_t)(s0 + s) * stride * D + d0);
-                const float w = lds_w[wave][s];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, x[j], acc[j]);
-            }
-            wave_lds_sync();
         }
     }
 #pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
+    for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m);
 #pragma unroll
-    for (int x = LPG; x < 64; x <<= 1)
+    for (int m = LPG; m < 64; m <<= 1)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], x);
+        for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], m);
+    if constexpr (WPR > 1) {
+        // the waves of the row sum their shares through LDS; wave 0 writes
+        lds_acc[sub][lane] = acc;
+        __syncthreads();
+        if (sub != 0) return;
+#pragma unroll
+        for (int w = 1; w < WPR; ++w) {
+            const f32x4 y = lds_acc[w][lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] += y[j];
+        }
+    }
 
     const bool empty = !(L > 0.f);
     const float inv = empty ? 0.f : 1.f / L;
-    if (g == 0 && d0 < a.Dv) {
+    if (lane < LPG && d0 < a.Dv) {
         uint16_t *outp = (uint16_t *)a.out + (q_token(a, b, i) * a.Hq + h) * a.Dv + d0;
         *(u32x2 *)outp = u32x2{pack2<DT>(acc[0] * inv, acc[1] * inv),
                                pack2<DT>(acc[2] * inv, acc[3] * inv)};
@@ -142,9 +171,16 @@ hipError_t launch_t(const KernelArgs &a, hipStream_t stream) {
     KernelArgs args = a;
     void *kargs[] = {&args};
     const long long nrows = (long long)a.B * a.Hq * a.qLen;
-    const unsigned blocks = (unsigned)((nrows + kRowsPerBlock - 1) / kRowsPerBlock);
-    return hipLaunchKernel((const void *)&combine_kernel<DT, D>, dim3(blocks),
-                           dim3(kRowsPerBlock * 64), kargs, 0, stream);
+    // partials per output row: the partitions of a fixed schedule, about
+    // grid / streams (+ 1) for the balanced one
+    const long long streams = (long long)a.B * a.head_blocks * a.row_blocks;
+    const long long per_row = a.schedule == kFixed ? a.S : a.S / (streams > 0 ? streams : 1) + 1;
+    const bool wide = per_row > 16;
+    const int rpb = wide ? 1 : kWaves;
+    const unsigned blocks = (unsigned)((nrows + rpb - 1) / rpb);
+    const void *fn = wide ? (const void *)&combine_kernel<DT, D, kWaves>
+                          : (const void *)&combine_kernel<DT, D, 1>;
+    return hipLaunchKernel(fn, dim3(blocks), dim3(kWaves * 64), kargs, 0, stream);
 }
 
 }  // namespace

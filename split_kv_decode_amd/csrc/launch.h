@@ -163,7 +163,10 @@ hipError_t launch_append(const KernelArgs &a, const void *k_new, const void *v_n
                          hipStream_t stream);
 
 // Query rows per kv head from which the matrix-core path is used (head dims
-// 64 or 128, Dk = Dv; every other head shape always takes it).
-constexpr int kMfmaMinRows = 32;
+// 64 or 128, Dk = Dv; every other head shape always takes it).  Measured: at
+// 8 rows (qLen 8, MHA) the matrix-core kernel streams 2.6 TB/s against the
+// VALU kernel's 1.9; at 4 rows the VALU kernel is ahead (6.4 against 6.0 TB/s
+// on the Qwen3-8B-shaped batch).
+constexpr int kMfmaMinRows = 8;
 
 }  // namespace mxfa

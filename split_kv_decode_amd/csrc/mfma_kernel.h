@@ -3,7 +3,7 @@
 //
 // Split-KV decode attention, matrix-core path (gfx950 MFMA).
 //
-// Used when a kv head carries many query rows (R = (Hq/Hkv) * qLen >= 32, e.g.
+// Used when a kv head carries several query rows (R = (Hq/Hkv) * qLen >= 8, e.g.
 // GQA groups times a multi-token draft): Q K^T and P V are then dense
 // contractions with 16-row tiles, which is how the ops-transformer articles
 // place FlashAttention on a matrix unit (Q K^T and P V on the cube unit,

@@ -304,7 +304,7 @@ def test_plan_covers_the_cache_exactly(shape, num_splits):
     B, Hq, Hkv, D, qLen, cap, causal, dt = shape
     p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits)
     assert p.rows == (Hq // Hkv) * qLen
-    if p.rows >= 32:
+    if p.rows >= 8:
         assert p.path == 1 and p.row_block == 64 and p.head_block == 1
     else:
         assert p.path == 0 and p.row_block in (1, 2, 4, 8) and p.row_block >= min(p.rows, 8)

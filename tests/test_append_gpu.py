@@ -83,7 +83,7 @@ def _run(inp, new_len, P=0, num_splits=0, use_ws=False, seed=1):
 CASES = [
     # (name, B, qLen, Hq, Hkv, D, cap, dtype, causal, lengths, new_len)
     ("valu_decode", 3, 1, 32, 8, 128, 1000, "bf16", False, [999, 500, 0], 1),
-    ("valu_draft", 3, 2, 8, 2, 64, 700, "fp16", True, [690, 33, 5], 5),
+    ("gqa_draft", 3, 2, 8, 2, 64, 700, "fp16", True, [690, 33, 5], 5),
     ("mfma_mtp", 2, 8, 64, 8, 128, 2048, "bf16", True, [2040, 100], 8),
     ("mfma_drop", 2, 8, 64, 8, 128, 2048, "bf16", True, [2045, 0], 8),
 ]

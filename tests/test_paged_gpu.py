@@ -63,7 +63,7 @@ def test_paged_shapes(shape, P):
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_paged_forced_splits(path, num_splits):
     if path == "valu":
-        w = wl.Workload("ps", B=3, qLen=2, Hq=8, Hkv=2, D=128, kv_cap=777, dtype="bf16",
+        w = wl.Workload("ps", B=3, qLen=2, Hq=4, Hkv=2, D=128, kv_cap=777, dtype="bf16",
                         causal=True, sigma=1.0, seed=17, len_range=(1, 777))
     else:
         w = wl.Workload("ps", B=3, qLen=4, Hq=16, Hkv=2, D=128, kv_cap=777, dtype="bf16",
