@@ -15,7 +15,15 @@ Hkv=8, D=128, bf16, KV cache of 16384 with per-sequence lengths uniform in
              launch / its mean duration from HIP events recorded around it on
              the stream it runs on, against the 8 TB/s HBM peak; traffic from
              a committed rocprofv3 counter summary when it matches this build;
-  cpu_baseline  the fp64 CPU oracle timed on this host on the same inputs.
+  cpu_baseline  the fp64 CPU oracle timed on this host on the same inputs
+             (median of up to 3 runs with every core it may use, and a
+             one-thread figure on a sample of the batch);
+  read_ceiling  the library's streaming-read probe over 2 GiB (nt and default
+             cache policy): the practical HBM read rate on this GPU.
+
+Caches smaller than 1 GiB are timed over rotating copies (enough that the
+copies together hold at least 1 GiB of K/V, at most 64), so that no call
+finds its K/V in the last-level cache left there by the previous one.
 """
 from __future__ import annotations
 
@@ -23,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -33,6 +42,8 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "qwen3_8b_decode"
 KERNEL_SOURCES = ["split_kv_decode_amd/csrc/split_valu.hip",
                   "split_kv_decode_amd/csrc/split_mfma.hip",
+                  "split_kv_decode_amd/csrc/split_mfma_wide.hip",
+                  "split_kv_decode_amd/csrc/mfma_kernel.h",
                   "split_kv_decode_amd/csrc/schedule.h",
                   "split_kv_decode_amd/csrc/device_common.h",
                   "split_kv_decode_amd/csrc/launch.h"]
@@ -264,6 +275,8 @@ def parse():
                          "(0 = the contiguous cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the 2 GiB streaming-read probe")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"),
@@ -315,19 +328,31 @@ def main():
         need = mx.workspace_size(w.B, w.Hq, w.Hkv, w.D, w.qLen, w.kv_cap, w.causal, dt,
                                  args.num_splits)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq, w.qLen), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    # rotating copies of q / K / V / out / lse (the block table and the
+    # lengths are shared)
+    kv = wl.kv_bytes(w, lens)
+    n_copies = max(1, min(MAX_COPIES, -(-ROTATE_BYTES // max(kv, 1))))
+    k0, v0 = (paged.k_pages, paged.v_pages) if P else (g.k_cache, g.v_cache)
+    sets = []
+    for c in range(n_copies):
+        kc, vc = (k0, v0) if c == 0 else (k0.clone(), v0.clone())
+        qc = q if c == 0 else q.clone()
+        sets.append((qc, kc, vc, torch.empty_like(q),
+                     torch.empty((w.B, w.Hq, w.qLen), dtype=torch.float32, device=dev)))
+    counter = [0]
+
     def call():
+        qc, kc, vc, oc, lc = sets[counter[0] % n_copies]
+        counter[0] += 1
         if P:
-            mx.fwd_kvcache_paged(q, paged.k_pages, paged.v_pages, paged.block_table,
-                                 paged.cache_seqlens, w.causal, out=out, lse=lse,
-                                 num_splits=args.num_splits, workspace=ws,
+            mx.fwd_kvcache_paged(qc, kc, vc, paged.block_table, paged.cache_seqlens, w.causal,
+                                 out=oc, lse=lc, num_splits=args.num_splits, workspace=ws,
                                  stream=stream.cuda_stream)
         else:
-            mx.fwd_kvcache(q, g.k_cache, g.v_cache, g.cache_seqlens, w.causal, out=out,
-                           lse=lse, num_splits=args.num_splits, workspace=ws,
+            mx.fwd_kvcache(qc, kc, vc, g.cache_seqlens, w.causal, out=oc, lse=lc,
+                           num_splits=args.num_splits, workspace=ws,
                            stream=stream.cuda_stream)
 
     for _ in range(args.warmup):
@@ -344,9 +369,10 @@ def main():
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
 
+    new_events = lambda: [(torch.cuda.Event(enable_timing=True),
+                           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     # split kernel alone: HIP events recorded around it on its stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = new_events()
     for a, b in evs:          # create the underlying HIP events
         a.record(stream)
         b.record(stream)
@@ -358,6 +384,16 @@ def main():
     torch.cuda.synchronize()
     split_ms = [a.elapsed_time(b) for a, b in evs]
     split_ms_mean = float(np.mean(split_ms))
+    # whole calls (split + merge), each between two events on the stream
+    cevs = new_events()
+    for a, b in cevs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    call_ms_median = statistics.median(a.elapsed_time(b) for a, b in cevs)
+
+    ceiling = read_ceiling(torch, mx, dev, stream) if not args.no_read_ceiling else None
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -368,7 +404,6 @@ def main():
         del src, dst
 
     alg_bytes = wl.algorithmic_bytes(w, lens)
-    kv = wl.kv_bytes(w, lens)
     q_bytes = w.B * w.qLen * w.Hq * w.D * w.elt
     # a paged cache also reads one block-table entry per page touched
     bt_bytes = sum(-(-max(0, min(n, w.kv_cap)) // P) for n in lens) * 4 if P else 0
@@ -380,21 +415,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        threads = args.cpu_threads or len(os.sched_getaffinity(0))
-        tc = time.perf_counter()
-        if P:
-            oracle.attention_paged(inp.q, paged_cpu.k_pages, paged_cpu.v_pages,
-                                   paged_cpu.block_table, paged_cpu.cache_seqlens, w.causal,
-                                   w.dtype, nthreads=threads)
-        else:
-            oracle.attention(inp.q, inp.k_cache, inp.v_cache, inp.cache_seqlens, w.causal,
-                             w.dtype, nthreads=threads)
-        cpu_s = time.perf_counter() - tc
-        cpu = {"value": round(alg_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": (f"the whole {w.name} batch, one call ({cpu_s:.2f} s; "
-                          f"{alg_bytes / 1e9:.3f} GB algorithmic)")}
+        cpu = cpu_baseline(args, w, inp, paged_cpu, lens, alg_bytes)
 
     rec = {
         "metric": "decode attention achieved HBM GB/s (% of peak) and attn-calls/s at B x KV len",
@@ -414,17 +435,104 @@ def main():
                    "causal": w.causal, "kv_layout": f"paged{P}" if P else "contiguous",
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "attn_calls_per_s": round(1e3 / ms_per_step, 1),
+        # one over the median event-timed call (split + merge kernels)
+        "attn_calls_per_s": round(1e3 / call_ms_median, 1),
+        "median_call_us": round(call_ms_median * 1e3, 2),
+        "wall_calls_per_s": round(1e3 / ms_per_step, 1),
+        "rotating_copies": n_copies,
         "plan": plan,
         "roofline": {"bound": "hbm", "kernel": SPLIT_KERNEL[plan["path"]],
                      "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(split_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "bytes_per_launch": split_bytes,
-                     "mean_launch_us": round(split_ms_mean * 1e3, 2)},
+                     "mean_launch_us": round(split_ms_mean * 1e3, 2),
+                     "median_launch_us": round(statistics.median(split_ms) * 1e3, 2),
+                     "frac_of_read_ceiling": (round(split_gbs / ceiling["nt_gbs"], 4)
+                                              if ceiling else None)},
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+ROTATE_BYTES = 1 << 30
+MAX_COPIES = 64
+READ_PROBE_BYTES = 1 << 31
+
+
+def read_ceiling(torch, mx, dev, stream, reps=10):
+    """Median rate of the library's streaming-read probe over 2 GiB, with the
+    attention kernels' nt load policy and with the default policy."""
+    src = torch.ones(READ_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {"kernel": "read_probe_kernel", "bytes": READ_PROBE_BYTES}
+    for nt in (True, False):
+        for _ in range(3):
+            mx.read_probe(src, nt, sink, cus, stream.cuda_stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            mx.read_probe(src, nt, sink, cus, stream.cuda_stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+        out["nt_gbs" if nt else "default_gbs"] = round(READ_PROBE_BYTES / (ms * 1e-3) / 1e9, 1)
+    del src
+    return out
+
+
+def time_oracle(fn, runs=3, long_s=5.0):
+    """Median wall time of up to `runs` calls (one if the first takes longer
+    than long_s seconds)."""
+    ts = []
+    for _ in range(runs):
+        t = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t)
+        if ts[0] > long_s:
+            break
+    return statistics.median(ts), len(ts)
+
+
+def cpu_baseline(args, w, inp, paged_cpu, lens, alg_bytes):
+    """The fp64 oracle on this host: the whole batch with every core this
+    process may use (median of up to 3 runs), and one thread on the first
+    sequences holding about an eighth of the K/V."""
+    import oracle
+    import workloads as wl
+    threads = args.cpu_threads or len(os.sched_getaffinity(0))
+    if paged_cpu is not None:
+        whole = lambda: oracle.attention_paged(inp.q, paged_cpu.k_pages, paged_cpu.v_pages,
+                                               paged_cpu.block_table, paged_cpu.cache_seqlens,
+                                               w.causal, w.dtype, nthreads=threads)
+    else:
+        whole = lambda: oracle.attention(inp.q, inp.k_cache, inp.v_cache, inp.cache_seqlens,
+                                         w.causal, w.dtype, nthreads=threads)
+    cpu_s, runs = time_oracle(whole)
+    # one thread: the first k sequences (contiguous cache)
+    total = sum(max(0, min(n, w.kv_cap)) for n in lens)
+    k, acc = 0, 0
+    while k < w.B and (k == 0 or acc * 8 < total):
+        acc += max(0, min(lens[k], w.kv_cap))
+        k += 1
+    sl = None if inp.cache_seqlens is None else inp.cache_seqlens[:k]
+    sub = wl.Workload(w.name, B=k, qLen=w.qLen, Hq=w.Hq, Hkv=w.Hkv, D=w.D, kv_cap=w.kv_cap,
+                      dtype=w.dtype, causal=w.causal, sigma=w.sigma, seed=w.seed,
+                      len_range=w.len_range)
+    sub_bytes = wl.algorithmic_bytes(sub, lens[:k])
+    one_s, one_runs = time_oracle(lambda: oracle.attention(
+        inp.q[:k], inp.k_cache[:k], inp.v_cache[:k], sl, w.causal, w.dtype, nthreads=1))
+    return {"value": round(alg_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"the whole {w.name} batch, one call per run, median of {runs} "
+                       f"({cpu_s:.2f} s; {alg_bytes / 1e9:.3f} GB algorithmic)"),
+            "one_thread": {"value": round(sub_bytes / one_s / 1e9, 4), "unit": "GB/s",
+                           "sample": (f"sequences 0..{k - 1} of the batch, contiguous cache, "
+                                      f"median of {one_runs} ({one_s:.2f} s; "
+                                      f"{sub_bytes / 1e9:.3f} GB algorithmic)")}}
 
 
 if __name__ == "__main__":

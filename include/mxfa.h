@@ -315,6 +315,23 @@ MXFA_API mxfa_status mxfa_last_plan(mxfa_plan_t *plan);
  * return MXFA_ERR_HIP. */
 MXFA_API mxfa_status mxfa_set_timing_events(void *before, void *after);
 
+/* Measurement helper, not part of attention: enqueues on `stream` one
+ * streaming read of `bytes` bytes at `src` in 16-byte buffer loads by
+ * num_cus * 2 workgroups of 256 threads (num_cus <= 0 means 256), each
+ * streaming its own contiguous share, consecutive lanes reading consecutive
+ * chunks.  nontemporal = 1 uses the
+ * cache policy of the attention kernels' K/V loads (the nt bit), 0 the
+ * default policy.  bytes / (duration between HIP events around the call) is
+ * the practical HBM read ceiling the attention kernels are compared with.
+ * src: device, 16-byte aligned, 0 < bytes <= 2^31, bytes a multiple of 16.
+ * sink: one device uint32 the kernel writes only if the xor of all the data
+ * equals a fixed pattern (it keeps the loads from being optimised away).
+ * Returns MXFA_ERR_INVALID_ARG for a bad argument (num_cus > 4096 included),
+ * MXFA_ERR_HIP if the launch fails. */
+MXFA_API mxfa_status mxfa_read_probe(const void *src, size_t bytes,
+                                     int nontemporal, uint32_t *sink,
+                                     int num_cus, void *stream);
+
 /* Static, human-readable text for a status value (never NULL). */
 MXFA_API const char *mxfa_status_string(int status);
 

@@ -24,7 +24,7 @@ EXPORTS = ("mxfa_fwd_kvcache", "mxfa_fwd_kvcache_ws", "mxfa_workspace_size",
            "mxfa_fwd_kvcache_append", "mxfa_fwd_kvcache_paged_append", "mxfa_fwd_varlen",
            "mxfa_fwd_kvcache_dkdv", "mxfa_workspace_size_dkdv",
            "mxfa_plan", "mxfa_last_plan", "mxfa_set_timing_events",
-           "mxfa_status_string", "mxfa_version")
+           "mxfa_read_probe", "mxfa_status_string", "mxfa_version")
 
 
 class Plan(ctypes.Structure):
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.mxfa_last_plan.restype = ci
     L.mxfa_set_timing_events.argtypes = [vp, vp]
     L.mxfa_set_timing_events.restype = ci
+    L.mxfa_read_probe.argtypes = [vp, sz, ci, vp, ci, vp]
+    L.mxfa_read_probe.restype = ci
     L.mxfa_status_string.argtypes = [ci]
     L.mxfa_status_string.restype = ctypes.c_char_p
     L.mxfa_version.argtypes = []
@@ -471,3 +473,19 @@ def workspace_size_dkdv(B, Hq, Hkv, Dk, Dv, qLen, kv_cap, causal=False, dtype=MX
     if st != MXFA_OK:
         raise MxfaError(st, "mxfa_workspace_size_dkdv")
     return n.value
+
+
+def read_probe(src, nontemporal: bool, sink, num_cus: int = 0, stream=None) -> None:
+    """Enqueue one streaming read of the whole device tensor `src` (the
+    practical read-ceiling kernel); `sink` is a device int32/uint32 tensor of
+    at least one element.  Time it with events on `stream`."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device).cuda_stream
+    nbytes = src.numel() * src.element_size()
+    with torch.cuda.device(src.device):
+        st = lib().mxfa_read_probe(ctypes.c_void_p(src.data_ptr()), nbytes, int(bool(nontemporal)),
+                                   ctypes.c_void_p(sink.data_ptr()), int(num_cus),
+                                   ctypes.c_void_p(stream))
+    if st != MXFA_OK:
+        raise MxfaError(st, "mxfa_read_probe")

@@ -361,3 +361,20 @@ def test_plan_rejects_bad_arguments():
     with pytest.raises(m.MxfaError):
         m.plan(1, 8, 2, 128, 1, 64, num_splits=-1)
     assert m.lib().mxfa_plan(1, 8, 2, 128, 1, 64, 0, 0, 0, 0, None) == INV
+
+
+@pytest.mark.parametrize("src,nbytes,nt,sink,cus", [
+    (0, 1 << 20, 1, 0x50000, 0),              # null source
+    (0x10000, 1 << 20, 1, 0, 0),              # null sink
+    (0x10008, 1 << 20, 1, 0x50000, 0),        # source not 16-byte aligned
+    (0x10000, 1 << 20, 1, 0x50002, 0),        # sink not 4-byte aligned
+    (0x10000, 0, 1, 0x50000, 0),              # nothing to read
+    (0x10000, 1000, 1, 0x50000, 0),           # not a multiple of 16 bytes
+    (0x10000, (1 << 31) + 16, 1, 0x50000, 0), # past 2^31 bytes
+    (0x10000, 1 << 20, 2, 0x50000, 0),        # policy flag not 0 / 1
+    (0x10000, 1 << 20, 0, 0x50000, 5000),     # absurd CU count
+])
+def test_read_probe_rejects_bad_arguments(src, nbytes, nt, sink, cus):
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    st = m.lib().mxfa_read_probe(vp(src), nbytes, nt, vp(sink), cus, None)
+    assert st == mxfa.MXFA_ERR_INVALID_ARG
