@@ -196,6 +196,10 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
         pl.path = MXFA_PATH_MFMA;
         pl.row_block = mfma_row_block(p.dk(), p.dv());
         pl.layout = kTokens;
+        // two kv heads per workgroup (two waves each) when Hkv is even: the
+        // workgroup then reads 512 contiguous bytes of every token row
+        // instead of 256
+        hpb = p.Hkv % kMfmaHeads == 0 ? kMfmaHeads : 1;
     } else {
         pl.path = MXFA_PATH_VALU;
         pl.row_block = next_pow2_le8((int)R);

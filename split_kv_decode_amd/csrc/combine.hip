@@ -175,7 +175,7 @@ hipError_t launch_t(const KernelArgs &a, hipStream_t stream) {
     // grid / streams (+ 1) for the balanced one
     const long long streams = (long long)a.B * a.head_blocks * a.row_blocks;
     const long long per_row = a.schedule == kFixed ? a.S : a.S / (streams > 0 ? streams : 1) + 1;
-    const bool wide = per_row > 16;
+    const bool wide = per_row > 24;
     const int rpb = wide ? 1 : kWaves;
     const unsigned blocks = (unsigned)((nrows + rpb - 1) / rpb);
     const void *fn = wide ? (const void *)&combine_kernel<DT, D, kWaves>

@@ -150,7 +150,8 @@ inline __host__ __device__ int mfma_row_block(int dk, int dv) {
     return (tk + tv <= 256 ? 4 : (tk + tv <= 320 ? 2 : 1)) * 16;
 }
 
-// Matrix-core split kernel: row_block = mfma_row_block(Dk, Dv), head_block 1.
+// Matrix-core split kernel: row_block = mfma_row_block(Dk, Dv), head_block 1
+// or 2 (dividing Hkv).
 hipError_t launch_split_mfma(const KernelArgs &a, int dtype, dim3 grid, hipStream_t stream);
 hipError_t launch_split_mfma_wide(const KernelArgs &a, int dtype, dim3 grid,
                                   hipStream_t stream);
@@ -168,5 +169,13 @@ hipError_t launch_append(const KernelArgs &a, const void *k_new, const void *v_n
 // VALU kernel's 1.9; at 4 rows the VALU kernel is ahead (6.4 against 6.0 TB/s
 // on the Qwen3-8B-shaped batch).
 constexpr int kMfmaMinRows = 8;
+// kv heads per workgroup of the matrix-core kernel (1 or 2).  Measured on the
+// Llama-70B-shaped MTP batch (537 MB of K/V): 2 heads take the split kernel
+// from 97.6 to 93.5 us and the whole call from 101.6 to 100.0 us (the merge
+// kernel reads twice the partials).
+#ifndef MXFA_MFMA_HEADS
+#define MXFA_MFMA_HEADS 2
+#endif
+constexpr int kMfmaHeads = MXFA_MFMA_HEADS;
 
 }  // namespace mxfa

@@ -10,13 +10,18 @@
 // softmax and scaling on the vector unit).  fp32 accumulation throughout.
 //
 // Work decomposition.  A workgroup of 4 waves (one per SIMD, one workgroup
-// per CU) serves a segment of one stream (sequence b, kv head, block of 64
-// query rows; schedules in schedule.h).  The segment is cut into tiles of 32
-// keys and wave w takes tiles w, w + 4, w + 8, ...: every wave holds all 64
-// rows (4 row tiles of 16) and its own online-softmax state, and streams its
-// tiles with no workgroup barrier.  Two tiles per wave are in flight in
-// registers.  At the end of the segment the 4 per-wave states are merged
-// through LDS with the same log-sum-exp rule as the split merge.
+// per CU) serves a segment of one stream (sequence b, block of HPW kv heads,
+// block of 64 query rows; schedules in schedule.h).  Each kv head of the
+// block gets WPH = 4 / HPW waves; the segment is cut into tiles of 32 keys
+// and the head's wave j takes tiles j, j + WPH, j + 2 WPH, ...: every wave
+// holds all 64 rows of its head (4 row tiles of 16) and its own online-
+// softmax state, and streams its tiles with no workgroup barrier, one tile in
+// flight in registers.  At the end of the segment the states of each head's
+// waves are merged through LDS with the same log-sum-exp rule as the split
+// merge.  With two heads per workgroup (the planner's choice when Hkv is
+// even) the workgroup reads 512 contiguous bytes of each token row of the
+// cache instead of 256, which streams measurably faster from HBM; the price
+// is twice as many partial results per row for the merge kernel.
 //
 // Per tile, with v_mfma_f32_16x16x32 (lane l = 16 g + p; A: row p, k-slice
 // 8g..8g+7; B: k-slice 8g..8g+7, column p; C: rows 4g..4g+3, column p):
@@ -108,7 +113,7 @@ __device__ __forceinline__ float group_sum(float x) {
 
 // DK / DV: the tile widths (padded head dims) of K and V; the real widths
 // a.Dk <= DK and a.Dv <= DV are multiples of 8.
-template <int DT, int DK, int DV, bool PAGED>
+template <int DT, int DK, int DV, int HPW, bool PAGED>
 struct Mfma {
     using T = MfmaType<DT>;
     typedef typename T::vec vec;
@@ -124,7 +129,8 @@ struct Mfma {
     static constexpr int LDV = kKT * NCHV / 64;   // V loads per lane per tile
     static constexpr int RT = MfmaShape<DK, DV>::RT;          // 16-row tiles per wave
     static constexpr int STG = MfmaShape<DK, DV>::kStages;    // LDS tile stages per wave
-    static constexpr int RB = RT * 16;            // query rows per workgroup
+    static constexpr int RB = RT * 16;            // query rows per workgroup and head
+    static constexpr int WPH = kMWaves / HPW;     // waves per kv head
     // XOR swizzle of the 16-byte chunks of a row by the key index, within
     // aligned groups of SW chunks (a power of two)
     static constexpr int SWK = (NCHK & (NCHK - 1)) == 0 ? NCHK : 8;
@@ -158,11 +164,11 @@ struct Mfma {
         return (uint32_t)((((src * RT + rt) * DB + db) * 64 + lane) * 16);
     }
 
-    __device__ static __forceinline__ void segment(const KernelArgs &a, Smem &sm, int b, int n, int kvh, int rb,
+    __device__ static __forceinline__ void segment(const KernelArgs &a, Smem &sm, int b, int n, int hb, int rb,
                                    int t_lo, int t_hi, int slot, bool whole) {
         b = __builtin_amdgcn_readfirstlane(b);
         n = __builtin_amdgcn_readfirstlane(n);
-        kvh = __builtin_amdgcn_readfirstlane(kvh);
+        hb = __builtin_amdgcn_readfirstlane(hb);
         rb = __builtin_amdgcn_readfirstlane(rb);
         t_lo = __builtin_amdgcn_readfirstlane(t_lo);
         t_hi = __builtin_amdgcn_readfirstlane(t_hi);
@@ -172,6 +178,10 @@ struct Mfma {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int g = lane >> 4;
         const int p = lane & 15;
+        // the wave's kv head (hx-th of the block) and its share of the tiles
+        const int hx = wave / WPH;
+        const int sub = wave % WPH;
+        const int kvh = hb * HPW + hx;
 
         // this sequence's query rows (fewer than R in a packed batch); keys
         // past t_end are invisible to every row of the block
@@ -189,7 +199,7 @@ struct Mfma {
         // first key of tile 0: a paged cache is read in page-aligned tiles
         const int t_base = PAGED ? (t_lo & ~(kKT - 1)) : t_lo;
         const int ntiles = t_end > t_lo ? (t_end - t_base + kKT - 1) / kKT : 0;
-        const int my_tiles = ntiles > wave ? (ntiles - wave + kMWaves - 1) / kMWaves : 0;
+        const int my_tiles = ntiles > sub ? (ntiles - sub + WPH - 1) / WPH : 0;
 
         // the lane's query row p of each row tile, as the B operand of S^T =
         // K Q^T; rows past R are zero and never written
@@ -244,7 +254,7 @@ struct Mfma {
         u32x4 ks[LDK], vs[LDV];
         // tile index of the wave's i-th tile; indices past the segment are
         // clamped to ntiles, whose keys all lie past t_end (loads read nothing)
-        auto tile_of = [&](int i) { return min(wave + kMWaves * i, ntiles); };
+        auto tile_of = [&](int i) { return min(sub + WPH * i, ntiles); };
         // paged: a tile (32 keys, aligned) lies in one page, or in two when the
         // page is 16 tokens; its block-table entries are read with vector
         // loads one tile ahead (tracked with the K/V loads, no scalar-cache
@@ -430,9 +440,10 @@ struct Mfma {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) l_run[rt] = group_sum(l_run[rt]);
 
-        // merge the 4 waves' states: the waves split the RT row tiles and
-        // their DB channel blocks between them (WPR waves per row tile, wave
-        // w takes row tile w % RT and the channel blocks w / RT + k * WPR)
+        // merge the states of each head's WPH waves: they split the RT row
+        // tiles and their DB channel blocks between them (wave sub of a head
+        // takes row tiles sub % RT + i * WPH, i < NRT, and, when a row tile
+        // has WPR > 1 waves, the channel blocks sub / RT + k * WPR)
         __syncthreads();                       // every wave is done with its V tiles
         if (g == 0) {
 #pragma unroll
@@ -446,71 +457,76 @@ struct Mfma {
 #pragma unroll
             for (int db = 0; db < DB; ++db) *(f32x4 *)(sm.buf + o_off(wave, rt, db, lane)) = o[rt][db];
         __syncthreads();
-        constexpr int WPR = kMWaves / RT;      // waves per row tile
-        constexpr int NDB = DB / WPR;          // channel blocks per wave
-        static_assert(kMWaves % RT == 0 && DB % WPR == 0, "merge split");
-        const int mrt = wave % RT;             // row tile this wave finishes
-        const int part = wave / RT;            // its share of the channel blocks
-        const int rloc = mrt * 16 + p;
-        float msrc[kMWaves];
-        float M = kNegInf;
+        constexpr int NRT = RT >= WPH ? RT / WPH : 1;   // row tiles per wave
+        constexpr int WPR = WPH > RT ? WPH / RT : 1;    // waves per row tile
+        constexpr int NDB = DB / WPR;                   // channel blocks per wave
+        static_assert((RT % WPH == 0 || WPH % RT == 0) && DB % WPR == 0, "merge split");
+        const int part = sub / RT;             // this wave's share of the channel blocks
+        const int src0 = hx * WPH;             // the head's first wave
 #pragma unroll
-        for (int w = 0; w < kMWaves; ++w) {
-            msrc[w] = sm.m[w][rloc];
-            M = fmaxf(M, msrc[w]);
-        }
-        float L = 0.f;
-        f32x4 acc[NDB];
+        for (int i = 0; i < NRT; ++i) {
+            const int mrt = sub % RT + i * WPH;
+            const int rloc = mrt * 16 + p;
+            float msrc[WPH];
+            float M = kNegInf;
 #pragma unroll
-        for (int k = 0; k < NDB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < WPH; ++w) {
+                msrc[w] = sm.m[src0 + w][rloc];
+                M = fmaxf(M, msrc[w]);
+            }
+            float L = 0.f;
+            f32x4 acc[NDB];
 #pragma unroll
-        for (int w = 0; w < kMWaves; ++w) {
-            const float sc = msrc[w] == kNegInf ? 0.f : fast_exp2(msrc[w] - M);
-            L += sc * sm.l[w][rloc];
+            for (int k = 0; k < NDB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < NDB; ++k)
-                acc[k] += sc * *(const f32x4 *)(sm.buf + o_off(w, mrt, part + k * WPR, lane));
-        }
-
-        // epilogue: the lane's row, channels 16 db + 4 g .. + 3 of its blocks
-        const int row = rb * RB + rloc;
-        if (row < Rb) {
-            const int qi = row / a.G;
-            const int qh = kvh * a.G + row % a.G;
-            const bool empty = !(L > 0.f);
-            const float inv = empty ? 0.f : 1.f / L;
-            const float lse2 = empty ? kNegInf : M + fast_log2(L);
-            if (whole) {
-                uint16_t *op = (uint16_t *)a.out + (q_token(a, b, qi) * a.Hq + qh) * a.Dv;
-#pragma unroll
-                for (int k = 0; k < NDB; ++k) {
-                    const int c0 = 16 * (part + k * WPR) + 4 * g;
-                    if (c0 < a.Dv)                 // channels past the head: not written
-                        *(u32x2 *)(op + c0) = u32x2{pack2<DT>(acc[k][0] * inv, acc[k][1] * inv),
-                                                    pack2<DT>(acc[k][2] * inv, acc[k][3] * inv)};
-                }
-                if (part == 0 && g == 0 && a.lse)
-                    a.lse[lse_index(a, b, qh, qi)] = empty ? kNegInf : lse2 * kLn2;
-            } else {
-                const size_t e = (size_t)slot * RB + rloc;   // head_block = 1
+            for (int w = 0; w < WPH; ++w) {
+                const float sc = msrc[w] == kNegInf ? 0.f : fast_exp2(msrc[w] - M);
+                L += sc * sm.l[src0 + w][rloc];
 #pragma unroll
                 for (int k = 0; k < NDB; ++k)
-                    *(f32x4 *)(a.ws_o + e * DV + 16 * (part + k * WPR) + 4 * g) = acc[k] * inv;
-                if (part == 0 && g == 0) a.ws_lse[e] = lse2;
+                    acc[k] += sc * *(const f32x4 *)(sm.buf + o_off(src0 + w, mrt, part + k * WPR, lane));
+            }
+
+            // epilogue: the lane's row, channels 16 db + 4 g .. + 3 of its blocks
+            const int row = rb * RB + rloc;
+            if (row < Rb) {
+                const int qi = row / a.G;
+                const int qh = kvh * a.G + row % a.G;
+                const bool empty = !(L > 0.f);
+                const float inv = empty ? 0.f : 1.f / L;
+                const float lse2 = empty ? kNegInf : M + fast_log2(L);
+                if (whole) {
+                    uint16_t *op = (uint16_t *)a.out + (q_token(a, b, qi) * a.Hq + qh) * a.Dv;
+#pragma unroll
+                    for (int k = 0; k < NDB; ++k) {
+                        const int c0 = 16 * (part + k * WPR) + 4 * g;
+                        if (c0 < a.Dv)                 // channels past the head: not written
+                            *(u32x2 *)(op + c0) = u32x2{pack2<DT>(acc[k][0] * inv, acc[k][1] * inv),
+                                                        pack2<DT>(acc[k][2] * inv, acc[k][3] * inv)};
+                    }
+                    if (part == 0 && g == 0 && a.lse)
+                        a.lse[lse_index(a, b, qh, qi)] = empty ? kNegInf : lse2 * kLn2;
+                } else {
+                    const size_t e = ((size_t)slot * HPW + hx) * RB + rloc;
+#pragma unroll
+                    for (int k = 0; k < NDB; ++k)
+                        *(f32x4 *)(a.ws_o + e * DV + 16 * (part + k * WPR) + 4 * g) = acc[k] * inv;
+                    if (part == 0 && g == 0) a.ws_lse[e] = lse2;
+                }
             }
         }
         __syncthreads();                       // the next segment reuses the LDS
     }
 };
 
-// One workgroup per CU, one wave per SIMD: each wave keeps the block's rows
+// One workgroup per CU, one wave per SIMD: each wave keeps its head's rows
 // of accumulators and one K/V tile in registers.
 
-template <int DT, int DK, int DV, int SCHED, bool PAGED>
+template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED>
 __global__ __launch_bounds__(kMWaves * 64)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_kv_mfma_kernel(KernelArgs a) {
-    using M = Mfma<DT, DK, DV, PAGED>;
+    using M = Mfma<DT, DK, DV, HPW, PAGED>;
     __shared__ __attribute__((aligned(16))) typename M::Smem sm;
     drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
                                  bool whole) {
@@ -518,20 +534,24 @@ void split_kv_mfma_kernel(KernelArgs a) {
     });
 }
 
+template <int DT, int DK, int DV, int HPW>
+const void *kernel_for(const KernelArgs &a) {
+    const bool paged = a.block_table != nullptr;
+    return a.schedule == kBalanced
+               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false>)
+               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false>);
+}
+
 template <int DT, int DK, int DV>
 hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
-    if (a.row_block != Mfma<DT, DK, DV, false>::RB || a.head_block != 1 || a.Dk > DK ||
-        a.Dv > DV)
+    if (a.row_block != Mfma<DT, DK, DV, 1, false>::RB || a.Dk > DK || a.Dv > DV ||
+        (a.head_block != 1 && a.head_block != 2) || a.Hkv % a.head_block != 0)
         return hipErrorInvalidValue;
     KernelArgs args = a;
     void *kargs[] = {&args};
-    const bool paged = a.block_table != nullptr;
-    const void *fn =
-        a.schedule == kBalanced
-            ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, kBalanced, true>
-                     : (const void *)&split_kv_mfma_kernel<DT, DK, DV, kBalanced, false>)
-            : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, kFixed, true>
-                     : (const void *)&split_kv_mfma_kernel<DT, DK, DV, kFixed, false>);
+    const void *fn = a.head_block == 2 ? kernel_for<DT, DK, DV, 2>(a) : kernel_for<DT, DK, DV, 1>(a);
     return hipLaunchKernel(fn, grid, dim3(kMWaves * 64), kargs, 0, stream);
 }
 

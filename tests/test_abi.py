@@ -305,10 +305,12 @@ def test_plan_covers_the_cache_exactly(shape, num_splits):
     p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits)
     assert p.rows == (Hq // Hkv) * qLen
     if p.rows >= 8:
-        assert p.path == 1 and p.row_block == 64 and p.head_block == 1
+        # matrix-core kernel: two kv heads per workgroup when Hkv is even
+        assert p.path == 1 and p.row_block == 64 and p.head_block == (2 if Hkv % 2 == 0 else 1)
     else:
         assert p.path == 0 and p.row_block in (1, 2, 4, 8) and p.row_block >= min(p.rows, 8)
-    assert p.head_block in (1, 4, 8, 16) and Hkv % p.head_block == 0
+        assert p.head_block in (1, 4, 8, 16)
+    assert Hkv % p.head_block == 0
     streams = B * (Hkv // p.head_block) * -(-p.rows // p.row_block)
     entry = p.head_block * p.row_block * (D + 1) * 4
     if p.schedule == 1:                      # balanced: planner's own choice only

@@ -125,6 +125,19 @@ def test_shape_sweep(D, dtype, G, qLen, causal):
     _full_check(inp)
 
 
+@pytest.mark.parametrize("Hkv,num_splits", [(1, 0), (3, 0), (2, 0), (6, 0), (4, 3), (5, 2)])
+def test_matrix_core_head_blocks(Hkv, num_splits):
+    """The matrix-core kernel with one kv head per workgroup (odd Hkv) and two
+    (even Hkv: two waves per head, merged per head), under the balanced and
+    forced partitions, ragged lengths and a causal draft."""
+    G = 8
+    w = wl.Workload("heads", B=3, qLen=2, Hq=G * Hkv, Hkv=Hkv, D=128, kv_cap=900, dtype="bf16",
+                    causal=True, sigma=1.0, seed=900 + Hkv, len_range=(1, 900))
+    inp = wl.make_inputs(w, lengths=[900, 333, 2])
+    _, _, plan = _full_check(inp, num_splits=num_splits)
+    assert plan["path"] == "mfma" and plan["head_block"] == (2 if Hkv % 2 == 0 else 1)
+
+
 @pytest.mark.parametrize("kvlen", [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 1025])
 def test_kv_length_sweep(kvlen):
     w = wl.Workload("lens", B=1, qLen=1, Hq=4, Hkv=1, D=128, kv_cap=kvlen, dtype="fp16",
