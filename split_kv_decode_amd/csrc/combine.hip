@@ -26,6 +26,7 @@
 // only the first Dv channels are written out.
 #include "device_common.h"
 #include "launch.h"
+#include "schedule.h"
 
 namespace mxfa {
 namespace {
@@ -47,7 +48,9 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(KernelArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int sub = wave % WPR;                 // this wave's share of the partials
-    const long long row = (long long)blockIdx.x * RPB + wave / WPR;
+    // rows in XCD order (schedule.h): a row is merged on the XCD whose
+    // workgroups wrote most of its partials
+    const long long row = (long long)xcd_order(blockIdx.x, gridDim.x) * RPB + wave / WPR;
     const long long nrows = (long long)a.B * a.Hq * a.qLen;
     if (row >= nrows) return;                   // whole wave exits together
     const int i = (int)(row % a.qLen);
