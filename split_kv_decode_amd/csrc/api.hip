@@ -196,10 +196,14 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
         pl.path = MXFA_PATH_MFMA;
         pl.row_block = mfma_row_block(p.dk(), p.dv());
         pl.layout = kTokens;
-        // two kv heads per workgroup (two waves each) when Hkv is even: the
-        // workgroup then reads 512 contiguous bytes of every token row
-        // instead of 256
-        hpb = p.Hkv % kMfmaHeads == 0 ? kMfmaHeads : 1;
+        // two kv heads per workgroup (two waves each) when Hkv is even and
+        // one row block holds all rows (decode): the workgroup then reads 512
+        // contiguous bytes of every token row instead of 256.  With several
+        // row blocks (prefill chunks) every block reads its head's K/V again
+        // from the caches, and pairing heads doubles what those re-reads
+        // cycle through: a packed chunked-prefill batch fell from 536 to 313
+        // TFLOP/s with pairs, so such problems keep one head per workgroup.
+        if (p.Hkv % kMfmaHeads == 0 && R <= pl.row_block) hpb = kMfmaHeads;
     } else {
         pl.path = MXFA_PATH_VALU;
         pl.row_block = next_pow2_le8((int)R);

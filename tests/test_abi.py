@@ -305,8 +305,10 @@ def test_plan_covers_the_cache_exactly(shape, num_splits):
     p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits)
     assert p.rows == (Hq // Hkv) * qLen
     if p.rows >= 8:
-        # matrix-core kernel: two kv heads per workgroup when Hkv is even
-        assert p.path == 1 and p.row_block == 64 and p.head_block == (2 if Hkv % 2 == 0 else 1)
+        # matrix-core kernel: two kv heads per workgroup when Hkv is even and
+        # one 64-row block holds every row
+        pair = Hkv % 2 == 0 and p.rows <= 64
+        assert p.path == 1 and p.row_block == 64 and p.head_block == (2 if pair else 1)
     else:
         assert p.path == 0 and p.row_block in (1, 2, 4, 8) and p.row_block >= min(p.rows, 8)
         assert p.head_block in (1, 4, 8, 16)

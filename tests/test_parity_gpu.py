@@ -138,6 +138,16 @@ def test_matrix_core_head_blocks(Hkv, num_splits):
     assert plan["path"] == "mfma" and plan["head_block"] == (2 if Hkv % 2 == 0 else 1)
 
 
+def test_matrix_core_many_rows_keep_one_head_per_workgroup():
+    """Several 64-row blocks per kv head (a prefill chunk): one kv head per
+    workgroup, whatever Hkv."""
+    w = wl.Workload("rows", B=2, qLen=20, Hq=16, Hkv=2, D=128, kv_cap=900, dtype="bf16",
+                    causal=True, sigma=1.0, seed=950, len_range=(1, 900))
+    inp = wl.make_inputs(w, lengths=[900, 25])
+    _, _, plan = _full_check(inp)
+    assert plan["path"] == "mfma" and plan["head_block"] == 1 and plan["rows"] == 160
+
+
 @pytest.mark.parametrize("kvlen", [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 1025])
 def test_kv_length_sweep(kvlen):
     w = wl.Workload("lens", B=1, qLen=1, Hq=4, Hkv=1, D=128, kv_cap=kvlen, dtype="fp16",
