@@ -343,19 +343,23 @@ def main():
         qc = q if c == 0 else q.clone()
         sets.append((qc, kc, vc, torch.empty_like(q),
                      torch.empty((w.B, w.Hq, w.qLen), dtype=torch.float32, device=dev)))
+    # each copy's call checked and marshalled once (PreparedCall); a step
+    # enqueues the next copy's call
+    if P:
+        calls = [mx.fwd_kvcache_paged(qc, kc, vc, paged.block_table, paged.cache_seqlens,
+                                      w.causal, out=oc, lse=lc, num_splits=args.num_splits,
+                                      workspace=ws, stream=stream.cuda_stream, prepare=True)
+                 for qc, kc, vc, oc, lc in sets]
+    else:
+        calls = [mx.fwd_kvcache(qc, kc, vc, g.cache_seqlens, w.causal, out=oc, lse=lc,
+                                num_splits=args.num_splits, workspace=ws,
+                                stream=stream.cuda_stream, prepare=True)
+                 for qc, kc, vc, oc, lc in sets]
     counter = [0]
 
     def call():
-        qc, kc, vc, oc, lc = sets[counter[0] % n_copies]
+        calls[counter[0] % n_copies].run()
         counter[0] += 1
-        if P:
-            mx.fwd_kvcache_paged(qc, kc, vc, paged.block_table, paged.cache_seqlens, w.causal,
-                                 out=oc, lse=lc, num_splits=args.num_splits, workspace=ws,
-                                 stream=stream.cuda_stream)
-        else:
-            mx.fwd_kvcache(qc, kc, vc, g.cache_seqlens, w.causal, out=oc, lse=lc,
-                           num_splits=args.num_splits, workspace=ws,
-                           stream=stream.cuda_stream)
 
     for _ in range(args.warmup):
         call()

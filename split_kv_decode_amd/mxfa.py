@@ -43,6 +43,31 @@ class Plan(ctypes.Structure):
         return d
 
 
+class PreparedCall:
+    """An attention call whose arguments were checked and marshalled once
+    (``fwd_kvcache(..., prepare=True)``, ``fwd_kvcache_paged(...,
+    prepare=True)``).  ``run()`` enqueues it again on the same stream with the
+    same tensors, whose contents may change between runs (a decode loop
+    writes the next query into ``q`` and bumps ``cache_seqlens`` in place);
+    it returns (out, lse).  The object keeps every tensor it points to alive."""
+    __slots__ = ("_fn", "_args", "_name", "_dev", "out", "lse", "_keep")
+
+    def __init__(self, fn, args, name, dev, out, lse, keep):
+        self._fn, self._args, self._name, self._dev = fn, args, name, dev
+        self.out, self.lse, self._keep = out, lse, keep
+
+    def run(self):
+        import torch
+        if torch.cuda.current_device() != self._dev:
+            with torch.cuda.device(self._dev):
+                st = self._fn(*self._args)
+        else:
+            st = self._fn(*self._args)
+        if st != MXFA_OK:
+            raise MxfaError(st, self._name)
+        return self.out, self.lse
+
+
 class MxfaError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
@@ -169,8 +194,9 @@ def _dtype_code(t) -> int:
 
 def fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
                 out=None, lse=None, return_lse: bool = True, num_splits: int = 0,
-                workspace=None, stream=None) -> Tuple[object, Optional[object]]:
-    """Decode attention on the current HIP stream; returns (out, lse).
+                workspace=None, stream=None, prepare: bool = False):
+    """Decode attention on the current HIP stream; returns (out, lse), or with
+    prepare=True a PreparedCall that enqueues the call on each run().
 
     q [B, qLen, Hq, D]; k_cache, v_cache [B, kv_cap, Hkv, D] (fp16 or bf16,
     contiguous, on one GPU); cache_seqlens int32 [B] or None.  With
@@ -211,31 +237,32 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     args = (ptr(q), ptr(k_cache), ptr(v_cache), ptr(cache_seqlens), ptr(out), ptr(lse),
             B, Hq, Hkv, D, qLen, kv_cap, int(bool(causal)), dt)
-    with torch.cuda.device(q.device):
-        if workspace is None and num_splits == 0:
-            st = lib().mxfa_fwd_kvcache(*args, ctypes.c_void_p(stream))
-        else:
-            if workspace is None:
+    if workspace is None and num_splits == 0:
+        fn, full = lib().mxfa_fwd_kvcache, (*args, ctypes.c_void_p(stream))
+    else:
+        if workspace is None:
+            with torch.cuda.device(q.device):
                 need = workspace_size(B, Hq, Hkv, D, qLen, kv_cap, causal, dt, num_splits)
-                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-            st = lib().mxfa_fwd_kvcache_ws(*args, int(num_splits), ptr(workspace),
-                                           workspace.numel() * workspace.element_size(),
-                                           ctypes.c_void_p(stream))
-    if st != MXFA_OK:
-        raise MxfaError(st, "mxfa_fwd_kvcache")
-    return out, lse
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        fn = lib().mxfa_fwd_kvcache_ws
+        full = (*args, int(num_splits), ptr(workspace),
+                workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    call = PreparedCall(fn, full, "mxfa_fwd_kvcache", q.device.index, out, lse,
+                        (q, k_cache, v_cache, cache_seqlens, workspace))
+    return call if prepare else call.run()
 
 
 def fwd_kvcache_paged(q, k_pages, v_pages, block_table, cache_seqlens=None,
                       causal: bool = False, out=None, lse=None, return_lse: bool = True,
-                      num_splits: int = 0, workspace=None,
-                      stream=None) -> Tuple[object, Optional[object]]:
+                      num_splits: int = 0, workspace=None, stream=None,
+                      prepare: bool = False):
     """Decode attention over a paged cache on the current HIP stream.
 
     q [B, qLen, Hq, D]; k_pages, v_pages [num_pages, page_size, Hkv, D];
     block_table int32 [B, max_pages] (token j of sequence b is row
     j % page_size of page block_table[b, j // page_size]); cache_seqlens
-    int32 [B] or None.  Returns (out, lse)."""
+    int32 [B] or None.  Returns (out, lse), or with prepare=True a
+    PreparedCall."""
     import torch
     for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -275,20 +302,20 @@ def fwd_kvcache_paged(q, k_pages, v_pages, block_table, cache_seqlens=None,
     args = (ptr(q), ptr(k_pages), ptr(v_pages), ptr(block_table), ptr(cache_seqlens),
             ptr(out), ptr(lse), B, Hq, Hkv, D, qLen, num_pages, page_size, max_pages,
             int(bool(causal)), dt)
-    with torch.cuda.device(q.device):
-        if workspace is None and num_splits == 0:
-            st = lib().mxfa_fwd_kvcache_paged(*args, ctypes.c_void_p(stream))
-        else:
-            if workspace is None:
+    if workspace is None and num_splits == 0:
+        fn, full = lib().mxfa_fwd_kvcache_paged, (*args, ctypes.c_void_p(stream))
+    else:
+        if workspace is None:
+            with torch.cuda.device(q.device):
                 need = workspace_size_paged(B, Hq, Hkv, D, qLen, page_size, max_pages, causal,
                                             dt, num_splits)
-                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-            st = lib().mxfa_fwd_kvcache_paged_ws(*args, int(num_splits), ptr(workspace),
-                                                 workspace.numel() * workspace.element_size(),
-                                                 ctypes.c_void_p(stream))
-    if st != MXFA_OK:
-        raise MxfaError(st, "mxfa_fwd_kvcache_paged")
-    return out, lse
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        fn = lib().mxfa_fwd_kvcache_paged_ws
+        full = (*args, int(num_splits), ptr(workspace),
+                workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    call = PreparedCall(fn, full, "mxfa_fwd_kvcache_paged", q.device.index, out, lse,
+                        (q, k_pages, v_pages, block_table, cache_seqlens, workspace))
+    return call if prepare else call.run()
 
 
 def fwd_kvcache_append(q, k_cache, v_cache, k_new, v_new, cache_seqlens, causal: bool = False,

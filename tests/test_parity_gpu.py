@@ -275,3 +275,41 @@ def test_workspace_errors_on_gpu():
     assert e.value.status == 3
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())          # untouched on error
+
+
+def test_prepared_call_reruns_with_new_contents():
+    """A PreparedCall enqueues the same call again: after the query and the
+    lengths change in place, its output equals a fresh call's, bit for bit,
+    and the oracle's; the paged variant likewise."""
+    import split_kv_decode_amd as mx
+    w = wl.Workload("prep", B=2, qLen=2, Hq=16, Hkv=2, D=128, kv_cap=700, dtype="bf16",
+                    causal=True, sigma=1.0, seed=61, len_range=(1, 700))
+    inp = wl.make_inputs(w, lengths=[700, 300])
+    g = inp.to("cuda")
+    call = mx.fwd_kvcache(g.q, g.k_cache, g.v_cache, g.cache_seqlens, True, prepare=True)
+    o1, l1 = call.run()
+    torch.cuda.synchronize()
+    first = o1.clone()
+    g.q.mul_(-1.0)
+    g.cache_seqlens.copy_(torch.tensor([650, 123], dtype=torch.int32))
+    o2, l2 = call.run()
+    f_o, f_l = mx.fwd_kvcache(g.q, g.k_cache, g.v_cache, g.cache_seqlens, True)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == o1.data_ptr() and not torch.equal(first, o2)
+    assert torch.equal(o2, f_o) and torch.equal(l2, f_l)
+    inp2 = wl.Inputs(w, g.q.cpu(), inp.k_cache, inp.v_cache,
+                     torch.tensor([650, 123], dtype=torch.int32), None)
+    ref_o, ref_l = parity.oracle_full(inp2)
+    parity.compare(o2.float().cpu().double().numpy(), l2.cpu().double().numpy(),
+                   ref_o, ref_l, "bf16", 0.0)
+    pg = wl.to_paged(inp2, 64).to("cuda")
+    pcall = mx.fwd_kvcache_paged(g.q, pg.k_pages, pg.v_pages, pg.block_table,
+                                 pg.cache_seqlens, True, prepare=True)
+    for _ in range(2):
+        po, pl = pcall.run()
+    fpo, fpl = mx.fwd_kvcache_paged(g.q, pg.k_pages, pg.v_pages, pg.block_table,
+                                    pg.cache_seqlens, True)
+    torch.cuda.synchronize()
+    assert torch.equal(po, fpo) and torch.equal(pl, fpl)
+    parity.compare(po.float().cpu().double().numpy(), pl.cpu().double().numpy(),
+                   ref_o, ref_l, "bf16", 0.0)
