@@ -277,6 +277,8 @@ def parse():
                          "(0 = the contiguous cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="rotating copies of the inputs (0 = enough for 1 GiB of K/V, <= 64)")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the 2 GiB streaming-read probe")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -335,7 +337,8 @@ def main():
     # rotating copies of q / K / V / out / lse (the block table and the
     # lengths are shared)
     kv = wl.kv_bytes(w, lens)
-    n_copies = max(1, min(MAX_COPIES, -(-ROTATE_BYTES // max(kv, 1))))
+    n_copies = (args.copies if args.copies > 0
+                else max(1, min(MAX_COPIES, -(-ROTATE_BYTES // max(kv, 1)))))
     k0, v0 = (paged.k_pages, paged.v_pages) if P else (g.k_cache, g.v_cache)
     sets = []
     for c in range(n_copies):

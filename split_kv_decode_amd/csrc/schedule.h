@@ -34,15 +34,24 @@ __device__ __forceinline__ long long uni(long long x) {
 }
 
 // Workgroups of a launch are handed to the GPU's 8 XCDs in turn (workgroup
-// i to XCD i % 8).  Share order of workgroup i in a grid of n: the shares
-// of one XCD are consecutive, so the partial results of a stream are written
-// by workgroups of one XCD, and the merge kernel (which orders its rows the
-// same way) reads each row's partials from the XCD that wrote them.  On the
+// i to XCD i % 8).  Share of workgroup i in a grid of n when shares
+// 0 .. nb - 1 hold all the work: XCD x takes shares floor(x nb / 8) ..
+// floor((x + 1) nb / 8) - 1, so the XCDs get equal work (within one share)
+// and one XCD's shares are consecutive; the partial results of a stream are
+// then written by
+// workgroups of one XCD, and the merge kernel (which orders its rows the same
+// way) reads each row's partials from the XCD that wrote them.  Workgroups
+// past those shares get share nb, which holds no work.  On the
 // Llama-70B-shaped MTP batch this takes the merge kernel from 6.3 to 5.0 us.
 constexpr int kXcds = 8;
-__device__ __forceinline__ int xcd_order(int i, int n) {
-    return n % kXcds == 0 ? (i % kXcds) * (n / kXcds) + i / kXcds : i;
+__device__ __forceinline__ int xcd_share(int i, int n, int nb) {
+    if (n % kXcds != 0) return i;
+    const int x = i % kXcds, k = i / kXcds;
+    const int lo = (int)((long long)x * nb / kXcds);
+    const int hi = (int)((long long)(x + 1) * nb / kXcds);
+    return k < hi - lo ? lo + k : nb;
 }
+__device__ __forceinline__ int xcd_order(int i, int n) { return xcd_share(i, n, n); }
 
 // Exclusive prefix sums of the clamped sequence lengths into cum[0..B]
 // (cum[B] = total), computed by the whole workgroup of 256 threads.
@@ -103,12 +112,14 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         long long W = (T + a.S - 1) / a.S;
         if (W < a.min_share) W = a.min_share;
         W = uni(W);
-        const int w = xcd_order(blockIdx.x, gridDim.x);
-        if (w == 0) {
+        if (blockIdx.x == 0) {
             for (int bb = threadIdx.x; bb <= a.B; bb += kScheduleThreads)
                 ((long long *)a.ws_cum)[bb] = cum[bb];
             if (threadIdx.x == 0) ((long long *)a.ws_cum)[a.B + 1] = W;
         }
+        // shares with work: fewer than the grid when W is held up by min_share
+        const int nb = (int)((T + W - 1) / W < a.S ? (T + W - 1) / W : a.S);
+        const int w = xcd_share(blockIdx.x, gridDim.x, nb);
         long long g = (long long)w * W;
         if (g >= T) return;
         const long long gend = g + W < T ? g + W : T;
