@@ -6,6 +6,8 @@ import os
 import re
 
 import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 import split_kv_decode_amd as m
 from split_kv_decode_amd import mxfa
@@ -301,8 +303,26 @@ SHAPES = [
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("num_splits", [0, 1, 2, 3, 7, 1000])
 def test_plan_covers_the_cache_exactly(shape, num_splits):
-    B, Hq, Hkv, D, qLen, cap, causal, dt = shape
-    p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits)
+    check_plan(*shape, num_splits)
+
+
+@settings(max_examples=400, deadline=None, derandomize=True)
+@given(B=st.integers(1, 70), G=st.sampled_from([1, 2, 3, 4, 5, 8, 16]),
+       Hkv=st.integers(1, 12), D=st.sampled_from([64, 128]), qLen=st.integers(1, 40),
+       cap=st.integers(0, 40000), causal=st.integers(0, 1), dt=st.integers(0, 1),
+       num_splits=st.sampled_from([0, 0, 0, 1, 2, 5, 64, 100000]),
+       cus=st.sampled_from([0, 80, 256, 304]))
+def test_plan_invariants_over_random_shapes(B, G, Hkv, D, qLen, cap, causal, dt, num_splits,
+                                            cus):
+    check_plan(B, G * Hkv, Hkv, D, qLen, cap, causal, dt, num_splits, cus)
+
+
+def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
+    """The plan routes the shape to the right kernel, covers every cache
+    position with a non-empty partition and sizes the scratch for every
+    partial result."""
+    p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus)
+    assert p.num_cus == (cus if cus > 0 else 256)
     assert p.rows == (Hq // Hkv) * qLen
     if p.rows >= 8:
         # matrix-core kernel: two kv heads per workgroup when Hkv is even and
@@ -318,6 +338,7 @@ def test_plan_covers_the_cache_exactly(shape, num_splits):
     if p.schedule == 1:                      # balanced: planner's own choice only
         assert num_splits == 0 and p.combine == 1 and p.chunk == 0
         assert (p.grid_x, p.grid_y, p.grid_z) == (p.num_splits, 1, 1)
+        assert p.grid_x == p.num_cus * (2 if p.path == 0 else 1)
         assert p.workspace_bytes >= (p.num_splits + streams) * entry + (B + 2) * 8
         return
     S, C = p.num_splits, p.chunk
