@@ -20,6 +20,7 @@ import numpy as np
 import torch
 
 import oracle
+import workloads
 
 OUT_TOL = {"fp16": 4e-3, "bf16": 2e-2}
 LSE_TOL = 1e-3
@@ -144,3 +145,60 @@ def oracle_paged(paged, inp):
     w = inp.workload
     return oracle.attention_paged(inp.q, paged.k_pages, paged.v_pages, paged.block_table,
                                   paged.cache_seqlens, w.causal, w.dtype)
+
+
+def bits16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy()
+
+
+def new_tokens(w, new_len, seed):
+    """k_new, v_new [B, new_len, Hkv, D] drawn N(0, sigma^2), rounded to the dtype."""
+    g = torch.Generator().manual_seed(seed)
+    mk = lambda: (torch.randn(w.B, new_len, w.Hkv, w.D, generator=g) * w.sigma).to(
+        w.torch_dtype)
+    return mk(), mk()
+
+
+def run_append(inp, new_len, P=0, num_splits=0, use_ws=False, seed=1):
+    """In-call KV append on the GPU (contiguous, or paged with pages of P)
+    checked against the oracle: the updated cache bit for bit, cache_seqlens
+    untouched, attention to tolerance.  Returns the grown lengths."""
+    import split_kv_decode_amd as mx
+    w = inp.workload
+    kn, vn = new_tokens(w, new_len, seed)
+    dev = "cuda"
+    dt = 1 if w.dtype == "bf16" else 0
+    if P:
+        pg = workloads.to_paged(inp, P, reserve=True)
+        kc, vc, bt, sl = (pg.k_pages.to(dev), pg.v_pages.to(dev), pg.block_table.to(dev),
+                          pg.cache_seqlens.to(dev))
+        k_ref, v_ref, lens = oracle.append_kv_paged(pg.k_pages, pg.v_pages, pg.block_table,
+                                                    kn, vn, pg.cache_seqlens)
+        if w.qLen:
+            ref_o, ref_l = oracle.attention_paged(inp.q, k_ref, v_ref, pg.block_table, lens,
+                                                  w.causal, w.dtype)
+        need = mx.workspace_size_paged(w.B, w.Hq, w.Hkv, w.D, w.qLen, P, bt.shape[1],
+                                       w.causal, dt, num_splits)
+    else:
+        kc, vc, bt = inp.k_cache.to(dev), inp.v_cache.to(dev), None
+        sl = inp.cache_seqlens.to(dev)
+        k_ref, v_ref, lens = oracle.append_kv(inp.k_cache, inp.v_cache, kn, vn,
+                                              inp.cache_seqlens)
+        if w.qLen:
+            ref_o, ref_l = oracle.attention(inp.q, k_ref, v_ref, lens, w.causal, w.dtype)
+        need = mx.workspace_size(w.B, w.Hq, w.Hkv, w.D, w.qLen, w.kv_cap, w.causal, dt,
+                                 num_splits)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev) if use_ws else None
+    sl_before = sl.clone()
+    out, lse = mx.fwd_kvcache_append(inp.q.to(dev), kc, vc, kn.to(dev), vn.to(dev), sl,
+                                     w.causal, num_splits=num_splits, workspace=ws,
+                                     block_table=bt)
+    torch.cuda.synchronize()
+    # the cache is updated bit for bit; cache_seqlens is left alone
+    assert np.array_equal(bits16(kc), k_ref.view(np.int16))
+    assert np.array_equal(bits16(vc), v_ref.view(np.int16))
+    assert torch.equal(sl, sl_before)
+    if w.qLen:
+        rep = compare(to_f64(out), lse.cpu().double().numpy(), ref_o, ref_l, w.dtype)
+        print(w.name, new_len, P, mx.last_plan().as_dict(), rep, flush=True)
+    return lens

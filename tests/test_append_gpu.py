@@ -26,60 +26,6 @@ def _gpu():
     oracle.build()
 
 
-def _bits(t):
-    return t.detach().cpu().contiguous().view(torch.int16).numpy()
-
-
-def _new_tokens(w, new_len, seed):
-    g = torch.Generator().manual_seed(seed)
-    mk = lambda: (torch.randn(w.B, new_len, w.Hkv, w.D, generator=g) * w.sigma).to(
-        w.torch_dtype)
-    return mk(), mk()
-
-
-def _run(inp, new_len, P=0, num_splits=0, use_ws=False, seed=1):
-    import split_kv_decode_amd as mx
-    w = inp.workload
-    kn, vn = _new_tokens(w, new_len, seed)
-    dev = "cuda"
-    dt = 1 if w.dtype == "bf16" else 0
-    if P:
-        pg = wl.to_paged(inp, P, reserve=True)
-        kc, vc, bt, sl = (pg.k_pages.to(dev), pg.v_pages.to(dev), pg.block_table.to(dev),
-                          pg.cache_seqlens.to(dev))
-        k_ref, v_ref, lens = oracle.append_kv_paged(pg.k_pages, pg.v_pages, pg.block_table,
-                                                    kn, vn, pg.cache_seqlens)
-        if w.qLen:
-            ref_o, ref_l = oracle.attention_paged(inp.q, k_ref, v_ref, pg.block_table, lens,
-                                                  w.causal, w.dtype)
-        need = mx.workspace_size_paged(w.B, w.Hq, w.Hkv, w.D, w.qLen, P, bt.shape[1],
-                                       w.causal, dt, num_splits)
-    else:
-        kc, vc, bt = inp.k_cache.to(dev), inp.v_cache.to(dev), None
-        sl = inp.cache_seqlens.to(dev)
-        k_ref, v_ref, lens = oracle.append_kv(inp.k_cache, inp.v_cache, kn, vn,
-                                              inp.cache_seqlens)
-        if w.qLen:
-            ref_o, ref_l = oracle.attention(inp.q, k_ref, v_ref, lens, w.causal, w.dtype)
-        need = mx.workspace_size(w.B, w.Hq, w.Hkv, w.D, w.qLen, w.kv_cap, w.causal, dt,
-                                 num_splits)
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev) if use_ws else None
-    sl_before = sl.clone()
-    out, lse = mx.fwd_kvcache_append(inp.q.to(dev), kc, vc, kn.to(dev), vn.to(dev), sl,
-                                     w.causal, num_splits=num_splits, workspace=ws,
-                                     block_table=bt)
-    torch.cuda.synchronize()
-    # the cache is updated bit for bit; cache_seqlens is left alone
-    assert np.array_equal(_bits(kc), k_ref.view(np.int16))
-    assert np.array_equal(_bits(vc), v_ref.view(np.int16))
-    assert torch.equal(sl, sl_before)
-    if w.qLen:
-        rep = parity.compare(parity.to_f64(out), lse.cpu().double().numpy(), ref_o, ref_l,
-                             w.dtype)
-        print(w.name, new_len, P, mx.last_plan().as_dict(), rep, flush=True)
-    return lens
-
-
 CASES = [
     # (name, B, qLen, Hq, Hkv, D, cap, dtype, causal, lengths, new_len)
     ("valu_decode", 3, 1, 32, 8, 128, 1000, "bf16", False, [999, 500, 0], 1),
@@ -96,7 +42,7 @@ def test_append_then_attend(case, P):
     w = wl.Workload(name, B=B, qLen=qLen, Hq=Hq, Hkv=Hkv, D=D, kv_cap=cap, dtype=dt,
                     causal=causal, sigma=1.0, seed=7 + P, len_range=(0, cap))
     inp = wl.make_inputs(w, lengths=lens)
-    got = _run(inp, new_len, P)
+    got = parity.run_append(inp, new_len, P)
     if P == 0:
         assert list(got) == [min(n + new_len, cap) for n in lens]
 
@@ -106,20 +52,20 @@ def test_append_forced_splits_and_caller_workspace(num_splits):
     w = wl.Workload("ws", B=2, qLen=4, Hq=32, Hkv=4, D=128, kv_cap=600, dtype="bf16",
                     causal=True, sigma=1.0, seed=31, len_range=(0, 600))
     inp = wl.make_inputs(w, lengths=[300, 596])
-    _run(inp, 4, 0, num_splits=num_splits, use_ws=True)
-    _run(inp, 4, 32, num_splits=num_splits, use_ws=True)
+    parity.run_append(inp, 4, 0, num_splits=num_splits, use_ws=True)
+    parity.run_append(inp, 4, 32, num_splits=num_splits, use_ws=True)
 
 
 def test_append_with_no_query_only_updates_the_cache():
     w = wl.Workload("q0", B=2, qLen=0, Hq=8, Hkv=2, D=64, kv_cap=64, dtype="fp16",
                     causal=False, sigma=1.0, seed=33, len_range=(0, 64))
     inp = wl.make_inputs(w, lengths=[10, 63])
-    _run(inp, 3, 0)
-    _run(inp, 3, 16)
+    parity.run_append(inp, 3, 0)
+    parity.run_append(inp, 3, 16)
 
 
 def test_append_nothing_is_plain_attention():
     w = wl.Workload("n0", B=2, qLen=2, Hq=8, Hkv=2, D=128, kv_cap=300, dtype="bf16",
                     causal=True, sigma=1.0, seed=35, len_range=(0, 300))
     inp = wl.make_inputs(w, lengths=[300, 7])
-    _run(inp, 0, 0)
+    parity.run_append(inp, 0, 0)

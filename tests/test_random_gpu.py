@@ -132,3 +132,24 @@ def test_random_packed_batches(case):
     rep = parity.compare(parity.to_f64(out), lse.cpu().double().numpy().T, ref_o, ref_l.T,
                          w.dtype)
     print(case, mx.last_plan().as_dict(), rep, flush=True)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_in_call_append(case):
+    """Random in-call appends (contiguous or paged caches, drafts of 1-8 new
+    tokens, sequences near capacity so some new tokens are dropped): the
+    cache bit for bit and the attention to tolerance."""
+    r = np.random.default_rng([SEED, 3000 + case])
+    B, G, Hkv = int(r.integers(1, 4)), int(r.choice([1, 4, 8])), int(r.integers(1, 3))
+    new_len = int(r.choice([1, 2, 5, 8]))
+    qLen = int(r.choice([0, 1, new_len]))
+    cap = int(r.integers(8, 1000))
+    lens = [int(x) for x in r.integers(0, cap + 1, size=B)]
+    w = wl.Workload(f"ra{case}", B=B, qLen=qLen, Hq=G * Hkv, Hkv=Hkv, D=int(r.choice([64, 128])),
+                    kv_cap=cap, dtype=str(r.choice(["fp16", "bf16"])),
+                    causal=bool(r.integers(0, 2)), sigma=1.0, seed=SEED + 3000 + case,
+                    len_range=(0, cap))
+    P = int(r.choice([0, 16, 64]))
+    print(f"case {case}: {w.describe()} lens={lens} new_len={new_len} page={P}", flush=True)
+    inp = wl.make_inputs(w, lengths=lens)
+    parity.run_append(inp, new_len, P, num_splits=int(r.choice([0, 0, 2])), seed=case)
