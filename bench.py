@@ -402,7 +402,8 @@ def main():
     torch.cuda.synchronize()
     call_ms_median = statistics.median(a.elapsed_time(b) for a, b in cevs)
 
-    ceiling = read_ceiling(torch, mx, dev, stream) if not args.no_read_ceiling else None
+    ceiling = (read_ceiling(torch, mx, dev, stream, kv) if not args.no_read_ceiling
+               else None)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -458,7 +459,10 @@ def main():
                      "mean_launch_us": round(split_ms_mean * 1e3, 2),
                      "median_launch_us": round(statistics.median(split_ms) * 1e3, 2),
                      "frac_of_read_ceiling": (round(split_gbs / ceiling["nt_gbs"], 4)
-                                              if ceiling else None)},
+                                              if ceiling else None),
+                     "frac_of_size_matched_ceiling": (
+                         round(split_gbs / ceiling["nt_gbs_at_workload_size"], 4)
+                         if ceiling and "nt_gbs_at_workload_size" in ceiling else None)},
         "read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
@@ -470,25 +474,40 @@ MAX_COPIES = 64
 READ_PROBE_BYTES = 1 << 31
 
 
-def read_ceiling(torch, mx, dev, stream, reps=10):
+def read_ceiling(torch, mx, dev, stream, size_bytes=0, reps=10):
     """Median rate of the library's streaming-read probe over 2 GiB, with the
-    attention kernels' nt load policy and with the default policy."""
+    attention kernels' nt load policy and with the default policy; and, when
+    size_bytes is given (the workload's K/V bytes), with the nt policy over
+    reads of that size taken from consecutive windows of the 2 GiB buffer (so
+    that no read finds its bytes in the last-level cache): the ceiling at the
+    workload's own size, where the ramp and tail of one pass weigh more."""
     src = torch.ones(READ_PROBE_BYTES, dtype=torch.uint8, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     out = {"kernel": "read_probe_kernel", "bytes": READ_PROBE_BYTES}
-    for nt in (True, False):
-        for _ in range(3):
-            mx.read_probe(src, nt, sink, cus, stream.cuda_stream)
+
+    def median_ms(views, nt):
+        for v in views[:3]:
+            mx.read_probe(v, nt, sink, cus, stream.cuda_stream)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
-        for a, b in evs:
+        for k, (a, b) in enumerate(evs):
             a.record(stream)
-            mx.read_probe(src, nt, sink, cus, stream.cuda_stream)
+            mx.read_probe(views[k % len(views)], nt, sink, cus, stream.cuda_stream)
             b.record(stream)
         torch.cuda.synchronize()
-        ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+        return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+    for nt in (True, False):
+        ms = median_ms([src], nt)
         out["nt_gbs" if nt else "default_gbs"] = round(READ_PROBE_BYTES / (ms * 1e-3) / 1e9, 1)
+    size = min(int(size_bytes) // 16 * 16, READ_PROBE_BYTES)
+    if size >= 1 << 20:
+        n = READ_PROBE_BYTES // size
+        views = [src[k * size:(k + 1) * size] for k in range(n)]
+        ms = median_ms(views, True)
+        out["workload_bytes"] = size
+        out["nt_gbs_at_workload_size"] = round(size / (ms * 1e-3) / 1e9, 1)
     del src
     return out
 
