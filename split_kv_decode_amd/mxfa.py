@@ -49,7 +49,10 @@ class PreparedCall:
     prepare=True)``).  ``run()`` enqueues it again on the same stream with the
     same tensors, whose contents may change between runs (a decode loop
     writes the next query into ``q`` and bumps ``cache_seqlens`` in place);
-    it returns (out, lse).  The object keeps every tensor it points to alive."""
+    it returns (out, lse).  The object keeps every tensor it points to alive;
+    the stream it was prepared for must outlive it.  Runs on one stream are
+    ordered like any other work there; the same PreparedCall must not run on
+    two streams at once (they would share its output and scratch)."""
     __slots__ = ("_fn", "_args", "_name", "_dev", "out", "lse", "_keep")
 
     def __init__(self, fn, args, name, dev, out, lse, keep):
