@@ -105,9 +105,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 #define MXFA_KV_LOAD_POLICY 2
 #endif
 
-// 16-byte load through a buffer descriptor (buffer_load_dwordx4).
+// 16-byte load through a buffer descriptor (buffer_load_dwordx4), with the
+// streaming policy above or, for K/V that other workgroups read again soon
+// (several row blocks of one kv head), the default one (POL = 0).
+template <int POL = MXFA_KV_LOAD_POLICY>
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, MXFA_KV_LOAD_POLICY);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, POL);
 }
 
 // Orders this wave's LDS accesses around a point where lanes exchange data

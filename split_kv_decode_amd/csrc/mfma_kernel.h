@@ -113,7 +113,9 @@ __device__ __forceinline__ float group_sum(float x) {
 
 // DK / DV: the tile widths (padded head dims) of K and V; the real widths
 // a.Dk <= DK and a.Dv <= DV are multiples of 8.
-template <int DT, int DK, int DV, int HPW, bool PAGED>
+// POL: cache policy of the K/V loads (the streaming one when each K/V byte
+// is read once; 0 when several row blocks of a head read it again).
+template <int DT, int DK, int DV, int HPW, bool PAGED, int POL = MXFA_KV_LOAD_POLICY>
 struct Mfma {
     using T = MfmaType<DT>;
     typedef typename T::vec vec;
@@ -285,7 +287,7 @@ struct Mfma {
             const uint32_t rng = valid <= 0 ? 0u : (uint32_t)min(valid, page) * tokb;
             const __amdgpu_buffer_rsrc_t r = make_rsrc(
                 (const uint16_t *)pool + ((size_t)pg << a.log_page) * row_elems, rng);
-            return load16(r, (uint32_t)(tok & (page - 1)) * tokb + lane_off);
+            return load16<POL>(r, (uint32_t)(tok & (page - 1)) * tokb + lane_off);
         };
         auto gload_v = [&](int j) {
             const int t0 = PAGED ? t_base + j * kKT : t_lo + j * kKT;
@@ -296,7 +298,7 @@ struct Mfma {
                     vs[u] = page_load(a.v, vtok, (size_t)a.Hkv * a.Dv, tok, pg_cur[tok - t0 >= 16],
                                       voff[u]);
                 else
-                    vs[u] = load16(vrsrc, (uint32_t)tok * vtok + voff[u]);
+                    vs[u] = load16<POL>(vrsrc, (uint32_t)tok * vtok + voff[u]);
             }
         };
         auto gload_k = [&](int j) {
@@ -308,7 +310,7 @@ struct Mfma {
                     ks[u] = page_load(a.k, ktok, (size_t)a.Hkv * a.Dk, tok, pg_cur[tok - t0 >= 16],
                                       koff[u]);
                 else
-                    ks[u] = load16(krsrc, (uint32_t)tok * ktok + koff[u]);
+                    ks[u] = load16<POL>(krsrc, (uint32_t)tok * ktok + koff[u]);
             }
         };
 
@@ -522,11 +524,11 @@ struct Mfma {
 // One workgroup per CU, one wave per SIMD: each wave keeps its head's rows
 // of accumulators and one K/V tile in registers.
 
-template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED>
+template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED, int POL>
 __global__ __launch_bounds__(kMWaves * 64)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_kv_mfma_kernel(KernelArgs a) {
-    using M = Mfma<DT, DK, DV, HPW, PAGED>;
+    using M = Mfma<DT, DK, DV, HPW, PAGED, POL>;
     __shared__ __attribute__((aligned(16))) typename M::Smem sm;
     drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
                                  bool whole) {
@@ -534,14 +536,14 @@ void split_kv_mfma_kernel(KernelArgs a) {
     });
 }
 
-template <int DT, int DK, int DV, int HPW>
+template <int DT, int DK, int DV, int HPW, int POL>
 const void *kernel_for(const KernelArgs &a) {
     const bool paged = a.block_table != nullptr;
     return a.schedule == kBalanced
-               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false>)
-               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false>);
+               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true, POL>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false, POL>)
+               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true, POL>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false, POL>);
 }
 
 template <int DT, int DK, int DV>
@@ -551,7 +553,11 @@ hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
         return hipErrorInvalidValue;
     KernelArgs args = a;
     void *kargs[] = {&args};
-    const void *fn = a.head_block == 2 ? kernel_for<DT, DK, DV, 2>(a) : kernel_for<DT, DK, DV, 1>(a);
+    // two kv heads per workgroup only with a single row block; several row
+    // blocks re-read each head's K/V, which then keep the default cache policy
+    const void *fn = a.head_block == 2    ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY>(a)
+                     : a.row_blocks > 1 ? kernel_for<DT, DK, DV, 1, 0>(a)
+                                        : kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY>(a);
     return hipLaunchKernel(fn, grid, dim3(kMWaves * 64), kargs, 0, stream);
 }
 
