@@ -195,6 +195,8 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
         // head shape only the matrix-core kernel's padded tiles hold
         pl.path = MXFA_PATH_MFMA;
         pl.row_block = mfma_row_block(p.dk(), p.dv());
+        if (MXFA_MFMA_SMALL && R <= kMfmaSmallRows && p.dk() <= 128 && p.dv() <= 128)
+            pl.row_block = kMfmaSmallRows;
         pl.layout = kTokens;
         // two kv heads per workgroup (two waves each) when Hkv is even and
         // one row block holds all rows (decode): the workgroup then reads 512
@@ -248,7 +250,8 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     long long slots;
     if (num_splits == 0 && S > 1 && p.B <= kMaxBalancedBatch) {
         pl.schedule = kBalanced;
-        const int P = num_cus * (pl.path == MXFA_PATH_MFMA ? kMfmaPerCU : kValuPerCU);
+        const int P = num_cus * (pl.path == MXFA_PATH_VALU ? kValuPerCU
+                                 : pl.row_block == kMfmaSmallRows ? 2 : kMfmaPerCU);
         pl.num_splits = P;
         pl.chunk = 0;
         pl.grid_x = P;

@@ -169,6 +169,13 @@ hipError_t launch_append(const KernelArgs &a, const void *k_new, const void *v_n
 // VALU kernel's 1.9; at 4 rows the VALU kernel is ahead (6.4 against 6.0 TB/s
 // on the Qwen3-8B-shaped batch).
 constexpr int kMfmaMinRows = 8;
+// At most 16 rows per kv head (e.g. GQA 8 with one query token): the
+// matrix-core kernel's small variant, one 16-row tile per wave and two
+// workgroups per CU (tile widths up to 128 x 128).
+#ifndef MXFA_MFMA_SMALL
+#define MXFA_MFMA_SMALL 1
+#endif
+constexpr int kMfmaSmallRows = 16;
 // kv heads per workgroup of the matrix-core kernel (1 or 2).  Measured on the
 // Llama-70B-shaped MTP batch (537 MB of K/V): 2 heads take the split kernel
 // from 97.6 to 93.5 us and the whole call from 101.6 to 100.0 us (the merge

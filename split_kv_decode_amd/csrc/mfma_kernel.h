@@ -51,6 +51,10 @@
 // last valid token.  Keys of the first tile that precede the segment are
 // masked.
 //
+// Few rows.  With at most 16 query rows per kv head (SMALL) a wave holds one
+// row tile and one LDS stage, about 200 registers and 74 KB of LDS per
+// workgroup, so two workgroups share a CU.
+//
 // Head dims.  The tile widths DK x DV (64 x 64, 128 x 128, 192 x 128 or
 // 256 x 256) hold any head dims Dk <= DK, Dv <= DV that are multiples of 8:
 // the Q channels past Dk are zero, the K and V chunks past the head read a
@@ -115,7 +119,10 @@ __device__ __forceinline__ float group_sum(float x) {
 // a.Dk <= DK and a.Dv <= DV are multiples of 8.
 // POL: cache policy of the K/V loads (the streaming one when each K/V byte
 // is read once; 0 when several row blocks of a head read it again).
-template <int DT, int DK, int DV, int HPW, bool PAGED, int POL = MXFA_KV_LOAD_POLICY>
+// SMALL: one row tile (16 rows) per wave and one LDS stage, for at most 16
+// query rows per kv head; two workgroups share a CU.
+template <int DT, int DK, int DV, int HPW, bool PAGED, int POL = MXFA_KV_LOAD_POLICY,
+          bool SMALL = false>
 struct Mfma {
     using T = MfmaType<DT>;
     typedef typename T::vec vec;
@@ -129,8 +136,8 @@ struct Mfma {
     static constexpr int VTB = kKT * ROWV;
     static constexpr int LDK = kKT * NCHK / 64;   // K loads per lane per tile
     static constexpr int LDV = kKT * NCHV / 64;   // V loads per lane per tile
-    static constexpr int RT = MfmaShape<DK, DV>::RT;          // 16-row tiles per wave
-    static constexpr int STG = MfmaShape<DK, DV>::kStages;    // LDS tile stages per wave
+    static constexpr int RT = SMALL ? 1 : MfmaShape<DK, DV>::RT;          // 16-row tiles per wave
+    static constexpr int STG = SMALL ? 1 : MfmaShape<DK, DV>::kStages;    // LDS tile stages per wave
     static constexpr int RB = RT * 16;            // query rows per workgroup and head
     static constexpr int WPH = kMWaves / HPW;     // waves per kv head
     // XOR swizzle of the 16-byte chunks of a row by the key index, within
@@ -524,11 +531,11 @@ struct Mfma {
 // One workgroup per CU, one wave per SIMD: each wave keeps its head's rows
 // of accumulators and one K/V tile in registers.
 
-template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED, int POL>
+template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED, int POL, bool SMALL>
 __global__ __launch_bounds__(kMWaves * 64)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1, SMALL ? 2 : 1)))
 void split_kv_mfma_kernel(KernelArgs a) {
-    using M = Mfma<DT, DK, DV, HPW, PAGED, POL>;
+    using M = Mfma<DT, DK, DV, HPW, PAGED, POL, SMALL>;
     __shared__ __attribute__((aligned(16))) typename M::Smem sm;
     drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
                                  bool whole) {
@@ -536,23 +543,32 @@ void split_kv_mfma_kernel(KernelArgs a) {
     });
 }
 
-template <int DT, int DK, int DV, int HPW, int POL>
+template <int DT, int DK, int DV, int HPW, int POL, bool SMALL = false>
 const void *kernel_for(const KernelArgs &a) {
     const bool paged = a.block_table != nullptr;
     return a.schedule == kBalanced
-               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true, POL>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false, POL>)
-               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true, POL>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false, POL>);
+               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true, POL, SMALL>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false, POL, SMALL>)
+               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true, POL, SMALL>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false, POL, SMALL>);
 }
 
 template <int DT, int DK, int DV>
 hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
-    if (a.row_block != Mfma<DT, DK, DV, 1, false>::RB || a.Dk > DK || a.Dv > DV ||
+    constexpr bool kHasSmall = DK + DV <= 256;
+    const bool small = kHasSmall && a.row_block == kMfmaSmallRows;
+    if ((!small && a.row_block != Mfma<DT, DK, DV, 1, false>::RB) || a.Dk > DK || a.Dv > DV ||
         (a.head_block != 1 && a.head_block != 2) || a.Hkv % a.head_block != 0)
         return hipErrorInvalidValue;
     KernelArgs args = a;
     void *kargs[] = {&args};
+    if constexpr (kHasSmall) {
+        if (small) {
+            const void *f = a.head_block == 2 ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY, true>(a)
+                                              : kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY, true>(a);
+            return hipLaunchKernel(f, grid, dim3(kMWaves * 64), kargs, 0, stream);
+        }
+    }
     // two kv heads per workgroup only with a single row block; several row
     // blocks re-read each head's K/V, which then keep the default cache policy
     const void *fn = a.head_block == 2    ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY>(a)

@@ -255,8 +255,12 @@ def test_plan_routes_head_dims():
     # 64 / 128 keep the VALU path for few rows; every other head shape takes
     # the matrix-core kernel with its padded tiles (fewer rows per block when wide)
     assert m.plan(4, 32, 8, 128, 1, 4096, 0, 1).path == 0
-    for D, rb in ((96, 64), (32, 64), (256, 16), (8, 64), (160, 16)):
+    # (4 rows per kv head: the small 16-row variant up to 128 x 128 tiles)
+    for D, rb in ((96, 16), (32, 16), (256, 16), (8, 16), (160, 16)):
         p = m.plan(4, 32, 8, D, 1, 4096, 0, 1)
+        assert p.path == 1 and p.row_block == rb, D
+    for D, rb in ((96, 64), (256, 16), (200, 16)):
+        p = m.plan(4, 64, 2, D, 2, 4096, 0, 1)                   # 64 rows per kv head
         assert p.path == 1 and p.row_block == rb, D
     n = ctypes.c_size_t()
     assert m.lib().mxfa_workspace_size_dkdv(2, 8, 2, 192, 128, 1, 64, 0, 0, -1,
@@ -325,10 +329,11 @@ def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
     assert p.num_cus == (cus if cus > 0 else 256)
     assert p.rows == (Hq // Hkv) * qLen
     if p.rows >= 8:
-        # matrix-core kernel: two kv heads per workgroup when Hkv is even and
-        # one 64-row block holds every row
-        pair = Hkv % 2 == 0 and p.rows <= 64
-        assert p.path == 1 and p.row_block == 64 and p.head_block == (2 if pair else 1)
+        # matrix-core kernel: 16-row blocks up to 16 rows, else 64; two kv
+        # heads per workgroup when Hkv is even and one block holds every row
+        rb = 16 if p.rows <= 16 else 64
+        pair = Hkv % 2 == 0 and p.rows <= rb
+        assert p.path == 1 and p.row_block == rb and p.head_block == (2 if pair else 1)
     else:
         assert p.path == 0 and p.row_block in (1, 2, 4, 8) and p.row_block >= min(p.rows, 8)
         assert p.head_block in (1, 4, 8, 16)
@@ -338,7 +343,7 @@ def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
     if p.schedule == 1:                      # balanced: planner's own choice only
         assert num_splits == 0 and p.combine == 1 and p.chunk == 0
         assert (p.grid_x, p.grid_y, p.grid_z) == (p.num_splits, 1, 1)
-        assert p.grid_x == p.num_cus * (2 if p.path == 0 else 1)
+        assert p.grid_x == p.num_cus * (2 if p.path == 0 or p.row_block == 16 else 1)
         assert p.workspace_bytes >= (p.num_splits + streams) * entry + (B + 2) * 8
         return
     S, C = p.num_splits, p.chunk
