@@ -190,7 +190,8 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     pl.rows = (int)R;
     int hpb = 1;
     const bool valu_dims = p.dk() == p.dv() && (p.dk() == 64 || p.dk() == 128);
-    if (R >= kMfmaMinRows || !valu_dims) {
+    const int mfma_min = p.dk() == 128 ? kMfmaMinRows128 : kMfmaMinRows;
+    if (R >= mfma_min || !valu_dims) {
         // many rows per kv head (Q K^T and P V are dense 16-row tiles), or a
         // head shape only the matrix-core kernel's padded tiles hold
         pl.path = MXFA_PATH_MFMA;

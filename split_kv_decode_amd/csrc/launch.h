@@ -164,11 +164,14 @@ hipError_t launch_append(const KernelArgs &a, const void *k_new, const void *v_n
                          hipStream_t stream);
 
 // Query rows per kv head from which the matrix-core path is used (head dims
-// 64 or 128, Dk = Dv; every other head shape always takes it).  Measured: at
-// 8 rows (qLen 8, MHA) the matrix-core kernel streams 2.6 TB/s against the
-// VALU kernel's 1.9; at 4 rows the VALU kernel is ahead (6.4 against 6.0 TB/s
-// on the Qwen3-8B-shaped batch).
+// 64 or 128, Dk = Dv; every other head shape always takes it): 4 at head dim
+// 128, 8 at 64.  Measured with the 16-row variant below against the VALU
+// kernel: at 4 rows and head dim 128 the Qwen3-8B batch 347-348 against
+// 351 us per call, the Qwen3-4B long batch 160.3 against 163.2, the SmallQ
+// q4 case 19.8 against 21.8; at head dim 64 (4 rows) the VALU kernel stays
+// ahead (189 against 199 us), and at 1-2 rows the two trade places by case.
 constexpr int kMfmaMinRows = 8;
+constexpr int kMfmaMinRows128 = 4;
 // At most 16 rows per kv head (e.g. GQA 8 with one query token): the
 // matrix-core kernel's small variant, one 16-row tile per wave and two
 // workgroups per CU (tile widths up to 128 x 128).

@@ -254,7 +254,9 @@ def test_dkdv_arguments_rejected_before_any_hip_call(kw, status):
 def test_plan_routes_head_dims():
     # 64 / 128 keep the VALU path for few rows; every other head shape takes
     # the matrix-core kernel with its padded tiles (fewer rows per block when wide)
-    assert m.plan(4, 32, 8, 128, 1, 4096, 0, 1).path == 0
+    assert m.plan(4, 32, 8, 64, 1, 4096, 0, 1).path == 0       # 4 rows, head dim 64
+    assert m.plan(4, 24, 8, 128, 1, 4096, 0, 1).path == 0      # 3 rows, head dim 128
+    assert m.plan(4, 32, 8, 128, 1, 4096, 0, 1).path == 1      # 4 rows, head dim 128
     # (4 rows per kv head: the small 16-row variant up to 128 x 128 tiles)
     for D, rb in ((96, 16), (32, 16), (256, 16), (8, 16), (160, 16)):
         p = m.plan(4, 32, 8, D, 1, 4096, 0, 1)
@@ -328,7 +330,7 @@ def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
     p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus)
     assert p.num_cus == (cus if cus > 0 else 256)
     assert p.rows == (Hq // Hkv) * qLen
-    if p.rows >= 8:
+    if p.rows >= (4 if D == 128 else 8):
         # matrix-core kernel: 16-row blocks up to 16 rows, else 64; two kv
         # heads per workgroup when Hkv is even and one block holds every row
         rb = 16 if p.rows <= 16 else 64

@@ -39,8 +39,9 @@ def _check(inp, P, num_splits=0, use_workspace=True, seed=0):
 
 # (name, B, qLen, Hq, Hkv, D, kv_cap, dtype, causal): every kernel layout
 SHAPES = [
-    ("valu_heads", 3, 1, 32, 8, 128, 1100, "bf16", False),     # all-heads slots
-    ("valu_tokens128", 3, 2, 4, 2, 128, 1100, "fp16", True),    # one head per workgroup
+    ("valu_heads", 3, 1, 16, 8, 128, 1100, "bf16", False),     # all-heads slots
+    ("valu_tokens128", 3, 2, 2, 2, 128, 1100, "fp16", True),    # one head per workgroup
+    ("mfma_small128", 3, 1, 32, 8, 128, 1100, "bf16", False),  # 4 rows: 16-row tiles
     ("valu_tokens64_r1", 2, 1, 2, 2, 64, 1100, "bf16", False),  # the capped load step
     ("valu_tokens64_r8", 2, 3, 4, 2, 64, 900, "fp16", True),
     ("mfma128", 2, 8, 16, 2, 128, 1100, "bf16", True),
@@ -63,7 +64,7 @@ def test_paged_shapes(shape, P):
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_paged_forced_splits(path, num_splits):
     if path == "valu":
-        w = wl.Workload("ps", B=3, qLen=2, Hq=4, Hkv=2, D=128, kv_cap=777, dtype="bf16",
+        w = wl.Workload("ps", B=3, qLen=2, Hq=2, Hkv=2, D=128, kv_cap=777, dtype="bf16",
                         causal=True, sigma=1.0, seed=17, len_range=(1, 777))
     else:
         w = wl.Workload("ps", B=3, qLen=4, Hq=16, Hkv=2, D=128, kv_cap=777, dtype="bf16",

@@ -178,7 +178,8 @@ def test_empty_rows_and_zero_lengths():
 
 
 @pytest.mark.parametrize("G,qLen,Hkv,D,cap,lengths", [
-    (4, 4, 2, 64, 3, [0, 1, 3]),          # VALU path, two row blocks of 8
+    (1, 6, 2, 64, 3, [0, 1, 3]),          # VALU path, one row block of 8
+    (4, 4, 2, 64, 3, [0, 1, 3]),          # matrix-core path, 16-row blocks
     (8, 16, 1, 128, 5, [0, 2, 5]),        # matrix-core path, two row blocks of 64
 ])
 def test_causal_draft_longer_than_the_cache(G, qLen, Hkv, D, cap, lengths):
