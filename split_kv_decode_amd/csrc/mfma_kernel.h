@@ -3,8 +3,9 @@
 //
 // Split-KV decode attention, matrix-core path (gfx950 MFMA).
 //
-// Used when a kv head carries several query rows (R = (Hq/Hkv) * qLen >= 8, e.g.
-// GQA groups times a multi-token draft): Q K^T and P V are then dense
+// Used when a kv head carries several query rows (R = (Hq/Hkv) * qLen of at
+// least 4 at head dim 128, 8 at 64; GQA groups times a multi-token draft):
+// Q K^T and P V are then dense
 // contractions with 16-row tiles, which is how the ops-transformer articles
 // place FlashAttention on a matrix unit (Q K^T and P V on the cube unit,
 // softmax and scaling on the vector unit).  fp32 accumulation throughout.
