@@ -87,15 +87,20 @@ __device__ __forceinline__ int clamp_to(int x, int lo, int hi) {
 // them) clamped to [0, kv_cap], plus the tokens appended in the call, at most
 // kv_cap; packed keys: cu_k[b + 1] - cu_k[b], offsets clamped into
 // [0, total_k] and the length to kv_cap.
-__device__ __forceinline__ int seq_len(const KernelArgs &a, int b) {
+// seq_len_from applies that rule to values already loaded: x0 = cu_k[b] and
+// x1 = cu_k[b + 1] for packed keys, x0 = cache_seqlens[b] otherwise (x1 unused).
+__device__ __forceinline__ int seq_len_from(const KernelArgs &a, int x0, int x1) {
     if (a.cu_k) {
-        const int lo = clamp_to(a.cu_k[b], 0, a.total_k);
-        const int hi = clamp_to(a.cu_k[b + 1], lo, a.total_k);
+        const int lo = clamp_to(x0, 0, a.total_k);
+        const int hi = clamp_to(x1, lo, a.total_k);
         return hi - lo < a.kv_cap ? hi - lo : a.kv_cap;
     }
-    const int n0 = a.seqlens ? a.seqlens[b] : a.kv_cap;
-    const int n = clamp_to(n0, 0, a.kv_cap);
+    const int n = clamp_to(a.seqlens ? x0 : a.kv_cap, 0, a.kv_cap);
     return a.new_len > a.kv_cap - n ? a.kv_cap : n + a.new_len;
+}
+__device__ __forceinline__ int seq_len(const KernelArgs &a, int b) {
+    if (a.cu_k) return seq_len_from(a, a.cu_k[b], a.cu_k[b + 1]);
+    return seq_len_from(a, a.seqlens ? a.seqlens[b] : 0, 0);
 }
 
 // First key row of sequence b in k / v (token rows of Hkv * D values).

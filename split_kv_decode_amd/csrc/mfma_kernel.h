@@ -149,15 +149,17 @@ struct Mfma {
     static_assert(NCHK % 8 == 0 && NCHV % 8 == 0, "loads of 4+ chunks stay in one key row group");
 
     // LDS: during the tile loop, STG K and V tile pairs per wave; during the
-    // merge, the 4 waves' O fragments (4 sources x RT row tiles x DB x 64
-    // lanes x f32x4).
+    // merge, each wave's RB x DV block of O as fp32 rows of ORS bytes (16
+    // bytes of padding, so the fragment stores of 16 rows hit distinct banks).
+    static constexpr int ORS = DV * 4 + 16;
     static constexpr int STAGE_BYTES = kMWaves * STG * (KTB + VTB);
-    static constexpr int MERGE_BYTES = kMWaves * RT * DB * 64 * 16;
+    static constexpr int MERGE_BYTES = kMWaves * RB * ORS;
     static constexpr int BUF_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
     struct Smem {
         uint8_t buf[BUF_BYTES];
         float m[kMWaves][RB];
         float l[kMWaves][RB];
+        float wt[kMWaves][RB];   // merge weight of each source wave's row
     };
 
     // the K and V tiles of stage `stage` of a wave, 16-byte chunks of a row
@@ -170,8 +172,8 @@ struct Mfma {
         return (uint32_t)((wave * STG + stage) * (KTB + VTB) + KTB + key * ROWV +
                           ((chunk ^ (key % SWV)) * 16));
     }
-    __device__ static uint32_t o_off(int src, int rt, int db, int lane) {
-        return (uint32_t)((((src * RT + rt) * DB + db) * 64 + lane) * 16);
+    __device__ static uint32_t o_off(int src, int row, int ch) {
+        return (uint32_t)((src * RB + row) * ORS + ch * 4);
     }
 
     __device__ static __forceinline__ void segment(const KernelArgs &a, Smem &sm, int b, int n, int hb, int rb,
@@ -210,27 +212,6 @@ struct Mfma {
         const int t_base = PAGED ? (t_lo & ~(kKT - 1)) : t_lo;
         const int ntiles = t_end > t_lo ? (t_end - t_base + kKT - 1) / kKT : 0;
         const int my_tiles = ntiles > sub ? (ntiles - sub + WPH - 1) / WPH : 0;
-
-        // the lane's query row p of each row tile, as the B operand of S^T =
-        // K Q^T; rows past R are zero and never written
-        vec qf[RT][KK];
-        int klim[RT];      // last key visible to the lane's row
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int row = rb * RB + rt * 16 + p;
-            const bool ok = row < Rb;
-            const int qi = ok ? row / a.G : 0;
-            const int qh = kvh * a.G + (ok ? row % a.G : 0);
-            klim[rt] = (a.causal && ok) ? min(t_end - 1, qi + n - qn) : t_end - 1;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                u32x4 x = {0, 0, 0, 0};
-                if (ok && 32 * kk + 8 * g < a.Dk)      // channels past the head: zero
-                    x = *(const u32x4 *)((const uint16_t *)a.q +
-                                         (q_token(a, b, qi) * a.Hq + qh) * a.Dk + 32 * kk + 8 * g);
-                qf[rt][kk] = __builtin_bit_cast(vec, x);
-            }
-        }
 
         // K/V of sequence b; the descriptor range ends with token t_end - 1,
         // so loads past it return zeros without touching memory
@@ -321,6 +302,36 @@ struct Mfma {
                     ks[u] = load16<POL>(krsrc, (uint32_t)tok * ktok + koff[u]);
             }
         };
+
+        // one tile in flight per wave: the first tile is requested before
+        // anything else, then Q is loaded while it streams; each later tile's
+        // loads are issued as soon as the tile before it is in LDS
+        if constexpr (PAGED) fetch_pages(tile_of(0), pg_cur);
+        gload_v(tile_of(0));
+        gload_k(tile_of(0));
+        if constexpr (PAGED) fetch_pages(tile_of(1), pg_cur);
+
+        // the lane's query row p of each row tile, as the B operand of S^T =
+        // K Q^T; rows past R are zero and never written
+        vec qf[RT][KK];
+        int klim[RT];      // last key visible to the lane's row
+        const size_t qtok0 = q_token(a, b, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int row = rb * RB + rt * 16 + p;
+            const bool ok = row < Rb;
+            const int qi = ok ? row / a.G : 0;
+            const int qh = kvh * a.G + (ok ? row % a.G : 0);
+            klim[rt] = (a.causal && ok) ? min(t_end - 1, qi + n - qn) : t_end - 1;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                u32x4 x = {0, 0, 0, 0};
+                if (ok && 32 * kk + 8 * g < a.Dk)      // channels past the head: zero
+                    x = *(const u32x4 *)((const uint16_t *)a.q +
+                                         ((qtok0 + qi) * a.Hq + qh) * a.Dk + 32 * kk + 8 * g);
+                qf[rt][kk] = __builtin_bit_cast(vec, x);
+            }
+        }
 
         // online softmax with a lazily moved reference: every lane keeps the
         // reference m of its row (the same in the row's 4 lanes) and a partial
@@ -435,12 +446,6 @@ struct Mfma {
                     o[rt][db] = T::mma(__builtin_bit_cast(vec, va), pb[rt], o[rt][db]);
             }
         };
-        // one tile in flight per wave: the next tile's loads are issued as
-        // soon as this tile is in LDS
-        if constexpr (PAGED) fetch_pages(tile_of(0), pg_cur);
-        gload_v(tile_of(0));
-        gload_k(tile_of(0));
-        if constexpr (PAGED) fetch_pages(tile_of(1), pg_cur);
         for (int i = 0; i < my_tiles; ++i) {
             const int j = tile_of(i);
             compute(STG == 2 ? (i & 1) : 0, j, tile_of(i + 1), tile_of(i + 2));
@@ -450,10 +455,9 @@ struct Mfma {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) l_run[rt] = group_sum(l_run[rt]);
 
-        // merge the states of each head's WPH waves: they split the RT row
-        // tiles and their DB channel blocks between them (wave sub of a head
-        // takes row tiles sub % RT + i * WPH, i < NRT, and, when a row tile
-        // has WPR > 1 waves, the channel blocks sub / RT + k * WPR)
+        // merge the states of each head's WPH waves: every wave leaves its
+        // rows of O and its (m, l) in LDS, then the head's waves split its RB
+        // rows (wave sub takes rows sub * RPW ..)
         __syncthreads();                       // every wave is done with its V tiles
         if (g == 0) {
 #pragma unroll
@@ -465,63 +469,67 @@ struct Mfma {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) *(f32x4 *)(sm.buf + o_off(wave, rt, db, lane)) = o[rt][db];
+            for (int db = 0; db < DB; ++db)
+                *(f32x4 *)(sm.buf + o_off(wave, rt * 16 + p, 16 * db + 4 * g)) = o[rt][db];
         __syncthreads();
-        constexpr int NRT = RT >= WPH ? RT / WPH : 1;   // row tiles per wave
-        constexpr int WPR = WPH > RT ? WPH / RT : 1;    // waves per row tile
-        constexpr int NDB = DB / WPR;                   // channel blocks per wave
-        static_assert((RT % WPH == 0 || WPH % RT == 0) && DB % WPR == 0, "merge split");
-        const int part = sub / RT;             // this wave's share of the channel blocks
+        constexpr int LPR = DV / 4;            // lanes per row
+        constexpr int RPI = 64 / LPR;          // rows per instruction
+        constexpr int RPW = RB / WPH;          // rows per wave
+        static_assert(RPW % RPI == 0 && RPW <= 64, "merge split");
         const int src0 = hx * WPH;             // the head's first wave
-#pragma unroll
-        for (int i = 0; i < NRT; ++i) {
-            const int mrt = sub % RT + i * WPH;
-            const int rloc = mrt * 16 + p;
-            float msrc[WPH];
+        // per row (lane j takes the wave's row j): the log-sum-exp rule gives
+        // each source wave the weight 2^(m_w - M) / L and the row its lse
+        if (lane < RPW) {
+            const int rloc = sub * RPW + lane;
             float M = kNegInf;
 #pragma unroll
-            for (int w = 0; w < WPH; ++w) {
-                msrc[w] = sm.m[src0 + w][rloc];
-                M = fmaxf(M, msrc[w]);
-            }
+            for (int w = 0; w < WPH; ++w) M = fmaxf(M, sm.m[src0 + w][rloc]);
+            float sc[WPH];
             float L = 0.f;
-            f32x4 acc[NDB];
-#pragma unroll
-            for (int k = 0; k < NDB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w = 0; w < WPH; ++w) {
-                const float sc = msrc[w] == kNegInf ? 0.f : fast_exp2(msrc[w] - M);
-                L += sc * sm.l[src0 + w][rloc];
-#pragma unroll
-                for (int k = 0; k < NDB; ++k)
-                    acc[k] += sc * *(const f32x4 *)(sm.buf + o_off(src0 + w, mrt, part + k * WPR, lane));
+                const float mw = sm.m[src0 + w][rloc];
+                sc[w] = mw == kNegInf ? 0.f : fast_exp2(mw - M);
+                L += sc[w] * sm.l[src0 + w][rloc];
             }
-
-            // epilogue: the lane's row, channels 16 db + 4 g .. + 3 of its blocks
+            const bool empty = !(L > 0.f);
+            const float inv = empty ? 0.f : 1.f / L;
+#pragma unroll
+            for (int w = 0; w < WPH; ++w) sm.wt[src0 + w][rloc] = sc[w] * inv;
             const int row = rb * RB + rloc;
             if (row < Rb) {
-                const int qi = row / a.G;
-                const int qh = kvh * a.G + row % a.G;
-                const bool empty = !(L > 0.f);
-                const float inv = empty ? 0.f : 1.f / L;
                 const float lse2 = empty ? kNegInf : M + fast_log2(L);
                 if (whole) {
-                    uint16_t *op = (uint16_t *)a.out + (q_token(a, b, qi) * a.Hq + qh) * a.Dv;
+                    if (a.lse)
+                        a.lse[lse_index(a, b, kvh * a.G + row % a.G, row / a.G)] =
+                            empty ? kNegInf : lse2 * kLn2;
+                } else {
+                    a.ws_lse[((size_t)slot * HPW + hx) * RB + rloc] = lse2;
+                }
+            }
+        }
+        wave_lds_sync();                       // the wave reads back its own weights
+        // then a lane takes 4 channels of a row, and the lanes of one store
+        // instruction cover RPI whole rows: results go out as contiguous runs
+        const int c0 = 4 * (lane % LPR);       // the lane's first channel
 #pragma unroll
-                    for (int k = 0; k < NDB; ++k) {
-                        const int c0 = 16 * (part + k * WPR) + 4 * g;
-                        if (c0 < a.Dv)                 // channels past the head: not written
-                            *(u32x2 *)(op + c0) = u32x2{pack2<DT>(acc[k][0] * inv, acc[k][1] * inv),
-                                                        pack2<DT>(acc[k][2] * inv, acc[k][3] * inv)};
-                    }
-                    if (part == 0 && g == 0 && a.lse)
-                        a.lse[lse_index(a, b, qh, qi)] = empty ? kNegInf : lse2 * kLn2;
+        for (int i = 0; i < RPW / RPI; ++i) {
+            const int rloc = sub * RPW + i * RPI + lane / LPR;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < WPH; ++w)
+                acc += sm.wt[src0 + w][rloc] * *(const f32x4 *)(sm.buf + o_off(src0 + w, rloc, c0));
+            const int row = rb * RB + rloc;
+            if (row < Rb) {
+                if (whole) {
+                    const int qi = row / a.G;
+                    const int qh = kvh * a.G + row % a.G;
+                    uint16_t *op = (uint16_t *)a.out + ((qtok0 + qi) * a.Hq + qh) * a.Dv;
+                    if (c0 < a.Dv)                     // channels past the head: not written
+                        *(u32x2 *)(op + c0) = u32x2{pack2<DT>(acc[0], acc[1]), pack2<DT>(acc[2], acc[3])};
                 } else {
                     const size_t e = ((size_t)slot * HPW + hx) * RB + rloc;
-#pragma unroll
-                    for (int k = 0; k < NDB; ++k)
-                        *(f32x4 *)(a.ws_o + e * DV + 16 * (part + k * WPR) + 4 * g) = acc[k] * inv;
-                    if (part == 0 && g == 0) a.ws_lse[e] = lse2;
+                    *(f32x4 *)(a.ws_o + e * DV + c0) = acc;
                 }
             }
         }

@@ -33,6 +33,10 @@ __device__ __forceinline__ long long uni(long long x) {
     return ((long long)hi << 32) | (unsigned)lo;
 }
 
+__device__ __forceinline__ const void *uni_ptr(const void *p) {
+    return (const void *)uni((long long)(uintptr_t)p);
+}
+
 // Workgroups of a launch are handed to the GPU's 8 XCDs in turn (workgroup
 // i to XCD i % 8).  Share of workgroup i in a grid of n when shares
 // 0 .. nb - 1 hold all the work: XCD x takes shares floor(x nb / 8) ..
@@ -53,6 +57,13 @@ __device__ __forceinline__ int xcd_share(int i, int n, int nb) {
 }
 __device__ __forceinline__ int xcd_order(int i, int n) { return xcd_share(i, n, n); }
 
+// x / d and x % d for 0 <= x, 0 < d, in 32-bit arithmetic when both fit
+// (the usual case; the 64-bit division costs several times as much)
+__device__ __forceinline__ long long div_nn(long long x, long long d) {
+    return (x <= 0x7fffffffLL && d <= 0x7fffffffLL) ? (long long)((uint32_t)x / (uint32_t)d)
+                                                      : x / d;
+}
+
 // Exclusive prefix sums of the clamped sequence lengths into cum[0..B]
 // (cum[B] = total), computed by the whole workgroup of 256 threads.
 __device__ __forceinline__ void length_prefix_sums(const KernelArgs &a, long long *cum,
@@ -60,12 +71,24 @@ __device__ __forceinline__ void length_prefix_sums(const KernelArgs &a, long lon
     constexpr int PER = (kMaxBalancedBatch + kScheduleThreads - 1) / kScheduleThreads;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
+    // every load is issued before any is used (one memory round trip); the
+    // descriptor ends with the array, so entries past it read 0
+    const int *src = a.cu_k ? a.cu_k : a.seqlens;
+    const uint32_t bytes = src ? (uint32_t)(a.cu_k ? a.B + 1 : a.B) * 4u : 0u;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(uni_ptr(src), (uint32_t)uni((int)bytes));
+    int x0[PER], x1[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t bb = (uint32_t)(t * PER + j);
+        x0[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(r, bb * 4u, 0, 0);
+        x1[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(r, bb * 4u + 4u, 0, 0);
+    }
     long long v[PER];
     long long mine = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int bb = t * PER + j;
-        v[j] = bb < a.B ? seq_len(a, bb) : 0;
+        v[j] = bb < a.B ? seq_len_from(a, x0[j], x1[j]) : 0;
         mine += v[j];
     }
     // inclusive scan of `mine` across the wave
@@ -109,7 +132,7 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         __shared__ long long wave_tot[kScheduleThreads / 64];
         length_prefix_sums(a, cum, wave_tot);
         const long long T = uni(cum[a.B] * HR);
-        long long W = (T + a.S - 1) / a.S;
+        long long W = div_nn(T + a.S - 1, a.S);
         if (W < a.min_share) W = a.min_share;
         W = uni(W);
         if (blockIdx.x == 0) {
@@ -118,7 +141,8 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
             if (threadIdx.x == 0) ((long long *)a.ws_cum)[a.B + 1] = W;
         }
         // shares with work: fewer than the grid when W is held up by min_share
-        const int nb = (int)((T + W - 1) / W < a.S ? (T + W - 1) / W : a.S);
+        const long long nbw = div_nn(T + W - 1, W);
+        const int nb = (int)(nbw < a.S ? nbw : a.S);
         const int w = xcd_share(blockIdx.x, gridDim.x, nb);
         long long g = (long long)w * W;
         if (g >= T) return;
@@ -132,8 +156,8 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         int b = uni(lo);
         int n = uni((int)(cum[b + 1] - cum[b]));
         const long long off = uni(g - cum[b] * HR);
-        int j = uni((int)(off / n));
-        int t = uni((int)(off % n));
+        int j = uni((int)div_nn(off, n));
+        int t = uni((int)(off - (long long)j * n));
         while (g < gend) {
             const int seg = (int)((long long)(n - t) < gend - g ? (long long)(n - t) : gend - g);
             segment(b, n, j / a.row_blocks, j % a.row_blocks, t, t + seg, (int)(w + b * HR + j),
