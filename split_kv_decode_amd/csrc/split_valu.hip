@@ -200,22 +200,6 @@ struct Valu {
         const bool row_ok = head_ok && my_row < Rb;
         const int causal_last = a.causal ? my_row / a.G + n - qn : INT32_MAX;
 
-        // Q rows of this lane's head, resident for the whole segment (16-bit)
-        u32x4 qr[RB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const int row = row0 + (r ^ phir);
-            if (head_ok && row < Rb) {
-                const int i = row / a.G;
-                const int h = kvh * a.G + row % a.G;
-                const uint16_t *qp = (const uint16_t *)a.q +
-                                     (q_token(a, b, i) * a.Hq + h) * D + 8 * sl;
-                qr[r] = *(const u32x4 *)qp;
-            } else {
-                qr[r] = u32x4{0, 0, 0, 0};
-            }
-        }
-
         // K/V of sequence b through buffer descriptors whose range ends with
         // token t_hi - 1: loads past the segment (the ragged end of the last
         // step, the prefetch after the final step) return zeros without
@@ -235,13 +219,6 @@ struct Valu {
             koff[u] = lane_base + (uint32_t)((u ^ phiu) * TSUB + ts) * tok_bytes;
             voff[u] = lane_base + (uint32_t)(u * TSUB + ts) * tok_bytes;
         }
-
-        float m_run = kNegInf, l_run = 0.f;
-        float o[RB][8];
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
 
         auto load_step = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[U]) {
             if constexpr (PAGED) {
@@ -274,6 +251,36 @@ struct Valu {
                 }
             }
         };
+
+        // the wave's first step is requested before Q is loaded
+        const int nmine = nsteps > ti ? (nsteps - ti + TI - 1) / TI : 0;
+        u32x4 kA[U], vA[U], kB[U], vB[U];
+        int st = ti;
+        load_step(st, kA, vA);
+
+        // Q rows of this lane's head, resident for the whole segment (16-bit)
+        u32x4 qr[RB];
+        const size_t qtok0 = q_token(a, b, 0);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int row = row0 + (r ^ phir);
+            if (head_ok && row < Rb) {
+                const int i = row / a.G;
+                const int h = kvh * a.G + row % a.G;
+                const uint16_t *qp = (const uint16_t *)a.q +
+                                     ((qtok0 + i) * a.Hq + h) * D + 8 * sl;
+                qr[r] = *(const u32x4 *)qp;
+            } else {
+                qr[r] = u32x4{0, 0, 0, 0};
+            }
+        }
+
+        float m_run = kNegInf, l_run = 0.f;
+        float o[RB][8];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
 
         auto compute_step = [&](int st, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
             float v[N];
@@ -344,10 +351,6 @@ struct Valu {
         // current one is computed (register double buffer).  Loads are
         // unconditional, so the wait counts stay exact.
         {
-            const int nmine = nsteps > ti ? (nsteps - ti + TI - 1) / TI : 0;
-            u32x4 kA[U], vA[U], kB[U], vB[U];
-            int st = ti;
-            load_step(st, kA, vA);
             for (int pair = 0; pair < nmine / 2; ++pair) {
                 load_step(st + TI, kB, vB);
                 compute_step(st, kA, vA);
