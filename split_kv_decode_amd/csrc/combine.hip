@@ -17,9 +17,10 @@
 // served by one workgroup was written directly by the split kernel and is
 // skipped; a stream with no token at all gets O = 0, lse = -inf here.  The
 // wave splits into NG groups of D/4 lanes (4 channels per lane, 16-byte
-// loads), each group taking every NG-th partition; the partitions' lse values
-// (one per lane) and the first 16 partition rows per lane are loaded
-// together, so the maximum and the weights cost no extra memory round trip.
+// loads), each group taking every NG-th partition; the lse values of the
+// first 128 partitions (two per lane) and the first 16 partition rows per
+// lane are loaded together, so the maximum and the weights cost no extra
+// memory round trip (with 4 waves per row that covers 128 partitions).
 // A partition's weight travels from its lane by a cross-lane read, and the
 // groups are summed with cross-lane exchanges.  D here is the channel count
 // of a partial row (the head dim, or the matrix-core kernel's padded V tile);
@@ -35,12 +36,15 @@ constexpr int kWaves = 4;                    // waves per workgroup
 
 // WPR waves per output row: 1 when rows have few partials, 4 (one workgroup
 // per row) when they have many, so that the partial rows of one output row
-// are read by 4 waves at once.
-template <int DT, int D, int WPR>
+// are read by 4 waves at once.  MANY (with WPR = 4): rows with more than 64
+// partials; each lane then holds two lse values and 16 partial rows in
+// flight, so up to 128 partials cost one memory round trip.
+template <int DT, int D, int WPR, bool MANY>
 __global__ __launch_bounds__(kWaves * 64) void combine_kernel(KernelArgs a) {
     constexpr int LPG = D / 4;                  // lanes per group
     constexpr int NG = 64 / LPG;                // groups per wave (1, 2 or 4)
-    constexpr int UNR = WPR == 1 ? 16 : 8;      // partial rows in flight per lane
+    constexpr int UNR = (WPR == 1 || MANY) ? 16 : 8;   // partial rows in flight per lane
+    constexpr int NLSE = MANY ? 128 : 64;       // partials whose lse the lanes hold
     constexpr int RPB = kWaves / WPR;           // rows per workgroup
     constexpr int STEP = WPR * NG;              // partials between a lane's loads
     __shared__ f32x4 lds_acc[WPR > 1 ? WPR : 1][64];
@@ -92,35 +96,43 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(KernelArgs a) {
     const int d0 = (lane % LPG) * 4;
     auto orow_of = [&](int s) { return *(const f32x4 *)(orow + (size_t)s * stride * D + d0); };
 
-    // the partials' lse (lane s holds partial s < 64) and the first UNR * STEP
-    // partial rows are loaded together, before the maximum is known
-    const float lv = lane < count ? lrow[(size_t)lane * stride] : kNegInf;
+    // the partials' lse (lane s holds partial s, and 64 + s with MANY) and the
+    // first UNR * STEP partial rows are loaded together, before the maximum
+    // is known
+    const float lv0 = lane < count ? lrow[(size_t)lane * stride] : kNegInf;
+    const float lv1 = MANY && lane + 64 < count ? lrow[(size_t)(lane + 64) * stride] : kNegInf;
     f32x4 x[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
         const int sp = g + u * STEP;
         x[u] = sp < count ? orow_of(sp) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    float M = lv;
-    for (int sp = lane + 64; sp < count; sp += 64) M = fmaxf(M, lrow[(size_t)sp * stride]);
+    float M = fmaxf(lv0, lv1);
+    for (int sp = lane + NLSE; sp < count; sp += 64) M = fmaxf(M, lrow[(size_t)sp * stride]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     if (M != kNegInf) {
-        // weight of partial s < 64 sits in lane s; -inf partials weigh 0
-        const float wl = fast_exp2(lv - M);
-        L = wl;
-        for (int sp = lane + 64; sp < count; sp += 64) L += fast_exp2(lrow[(size_t)sp * stride] - M);
+        // weights of partials s < NLSE sit in lane s % 64; -inf partials weigh 0
+        const float w0 = fast_exp2(lv0 - M);
+        const float w1 = MANY ? fast_exp2(lv1 - M) : 0.f;
+        L = w0 + w1;
+        for (int sp = lane + NLSE; sp < count; sp += 64) L += fast_exp2(lrow[(size_t)sp * stride] - M);
+        // every lane takes part in the cross-lane reads
+        auto add = [&](int sp, const f32x4 &xs) {
+            const float wa = __shfl(w0, sp & 63);
+            const float wb = MANY ? __shfl(w1, sp & 63) : 0.f;
+            if (sp < count) {
+                const float w = sp < 64 ? wa
+                                        : (sp < NLSE ? wb : fast_exp2(lrow[(size_t)sp * stride] - M));
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int sp = g + u * STEP;
-            const float w = __shfl(wl, sp & 63);
-            if (sp < count)
+                for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, xs[j], acc[j]);
+            }
+        };
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, x[u][j], acc[j]);
-        }
+        for (int u = 0; u < UNR; ++u) add(g + u * STEP, x[u]);
         // more partials than the first batch holds
         for (int s0 = UNR * STEP; s0 < count; s0 += UNR * STEP) {
 #pragma unroll
@@ -129,15 +141,7 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(KernelArgs a) {
                 x[u] = sp < count ? orow_of(sp) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int sp = s0 + g + u * STEP;
-                const float ws = __shfl(wl, sp & 63);      // every lane takes part
-                if (sp < count) {
-                    const float w = sp < 64 ? ws : fast_exp2(lrow[(size_t)sp * stride] - M);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, x[u][j], acc[j]);
-                }
-            }
+            for (int u = 0; u < UNR; ++u) add(s0 + g + u * STEP, x[u]);
         }
     }
 #pragma unroll
@@ -178,11 +182,21 @@ hipError_t launch_t(const KernelArgs &a, hipStream_t stream) {
     // grid / streams (+ 1) for the balanced one
     const long long streams = (long long)a.B * a.head_blocks * a.row_blocks;
     const long long per_row = a.schedule == kFixed ? a.S : a.S / (streams > 0 ? streams : 1) + 1;
+    // the balanced schedule's busy shares are at most the grid and at most
+    // the largest total the lengths allow over the share floor
+    long long busy = a.S;
+    if (a.schedule != kFixed && a.min_share > 0) {
+        const long long most = (streams * a.kv_cap + a.min_share - 1) / a.min_share;
+        if (most < busy) busy = most;
+    }
+    const long long most_per_row = a.schedule == kFixed ? a.S : busy / (streams > 0 ? streams : 1) + 1;
+    // the grid-based count also decides when few rows need more workgroups
     const bool wide = per_row > 24;
     const int rpb = wide ? 1 : kWaves;
     const unsigned blocks = (unsigned)((nrows + rpb - 1) / rpb);
-    const void *fn = wide ? (const void *)&combine_kernel<DT, D, kWaves>
-                          : (const void *)&combine_kernel<DT, D, 1>;
+    const void *fn = !wide               ? (const void *)&combine_kernel<DT, D, 1, false>
+                     : most_per_row > 64 ? (const void *)&combine_kernel<DT, D, kWaves, true>
+                                         : (const void *)&combine_kernel<DT, D, kWaves, false>;
     return hipLaunchKernel(fn, dim3(blocks), dim3(kWaves * 64), kargs, 0, stream);
 }
 
