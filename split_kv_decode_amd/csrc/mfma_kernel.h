@@ -53,7 +53,7 @@
 // masked.
 //
 // Few rows.  With at most 16 query rows per kv head (SMALL) a wave holds one
-// row tile and one LDS stage, about 200 registers and 74 KB of LDS per
+// row tile and one LDS stage, about 215 registers and 73 KB of LDS per
 // workgroup, so two workgroups share a CU.
 //
 // Head dims.  The tile widths DK x DV (64 x 64, 128 x 128, 192 x 128 or
