@@ -122,8 +122,12 @@ __device__ __forceinline__ float group_sum(float x) {
 // is read once; 0 when several row blocks of a head read it again).
 // SMALL: one row tile (16 rows) per wave and one LDS stage, for at most 16
 // query rows per kv head; two workgroups share a CU.
+// KD: K is loaded from memory straight into the matrix operand layout (16
+// keys x 64 bytes per load instruction) instead of through LDS; used when
+// several row blocks of a head re-read its K/V from the caches, where the LDS
+// round trip, not the memory access pattern, is what limits the kernel.
 template <int DT, int DK, int DV, int HPW, bool PAGED, int POL = MXFA_KV_LOAD_POLICY,
-          bool SMALL = false>
+          bool SMALL = false, bool KD = false>
 struct Mfma {
     using T = MfmaType<DT>;
     typedef typename T::vec vec;
@@ -228,12 +232,20 @@ struct Mfma {
         // from the first key of its instruction (kfirst(u) = 64 u / NCH);
         // chunks past the head's width read chunk 0 again (their Q channels
         // are zero and their O channels are never written).
+        // With KD, load (kb, kk) of a tile gives lane (g, p) the 16 bytes of
+        // key 16 kb + p, chunk 4 kk + g: exactly its slice of the A operand
+        // of S^T = K Q^T; koff[kk] is the lane's offset from key 16 kb.
         uint32_t koff[LDK], voff[LDV];
 #pragma unroll
         for (int u = 0; u < LDK; ++u) {
-            const int f = 64 * u + lane, key = f / NCHK, ch = f % NCHK;
-            koff[u] = (uint32_t)(key - 64 * u / NCHK) * ktok + (uint32_t)kvh * a.Dk * 2 +
-                      16u * (8 * ch < a.Dk ? ch : 0);
+            if constexpr (KD) {
+                const int ch = 4 * (u % KK) + g;
+                koff[u] = (uint32_t)p * ktok + (uint32_t)kvh * a.Dk * 2 + 16u * (8 * ch < a.Dk ? ch : 0);
+            } else {
+                const int f = 64 * u + lane, key = f / NCHK, ch = f % NCHK;
+                koff[u] = (uint32_t)(key - 64 * u / NCHK) * ktok + (uint32_t)kvh * a.Dk * 2 +
+                          16u * (8 * ch < a.Dk ? ch : 0);
+            }
         }
 #pragma unroll
         for (int u = 0; u < LDV; ++u) {
@@ -294,7 +306,7 @@ struct Mfma {
             const int t0 = PAGED ? t_base + j * kKT : t_lo + j * kKT;
 #pragma unroll
             for (int u = 0; u < LDK; ++u) {
-                const int tok = t0 + 64 * u / NCHK;
+                const int tok = KD ? t0 + 16 * (u / KK) : t0 + 64 * u / NCHK;
                 if constexpr (PAGED)
                     ks[u] = page_load(a.k, ktok, (size_t)a.Hkv * a.Dk, tok, pg_cur[tok - t0 >= 16],
                                       koff[u]);
@@ -351,12 +363,15 @@ struct Mfma {
             const int key0 = t_base + j * kKT;
             // paged: keys of the first tile before t_lo are not part of the segment
             const int vis_lo = (PAGED && key0 < t_lo) ? t_lo - key0 - 4 * g : INT32_MIN;
-            // stage this tile's K and V rows in the wave's LDS buffer `set`
+            // stage this tile's K (without KD) and V rows in the wave's LDS
+            // buffer `set`; the next tile streams while this one is computed
+            if constexpr (!KD) {
 #pragma unroll
-            for (int u = 0; u < LDK; ++u)
-                *(u32x4 *)(sm.buf + k_off(wave, set, (64 * u + lane) / NCHK, (64 * u + lane) % NCHK)) =
-                    ks[u];
-            gload_k(jn);       // the next tile streams while this one is computed
+                for (int u = 0; u < LDK; ++u)
+                    *(u32x4 *)(sm.buf + k_off(wave, set, (64 * u + lane) / NCHK, (64 * u + lane) % NCHK)) =
+                        ks[u];
+                gload_k(jn);
+            }
             uint32_t pg_nxt[2];
             if constexpr (PAGED) fetch_pages(jnn, pg_nxt);
 #pragma unroll
@@ -364,7 +379,7 @@ struct Mfma {
                 *(u32x4 *)(sm.buf + v_off(wave, set, (64 * u + lane) / NCHV, (64 * u + lane) % NCHV)) =
                     vs[u];
             gload_v(jn);
-            if constexpr (PAGED) {
+            if constexpr (PAGED && !KD) {
                 pg_cur[0] = pg_nxt[0];
                 pg_cur[1] = pg_nxt[1];
             }
@@ -376,8 +391,9 @@ struct Mfma {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    ka[kb][kk] = __builtin_bit_cast(
-                        vec, *(const u32x4 *)(sm.buf + k_off(wave, set, 16 * kb + p, 4 * kk + g)));
+                    ka[kb][kk] = KD ? __builtin_bit_cast(vec, ks[kb * KK + kk])
+                                    : __builtin_bit_cast(vec, *(const u32x4 *)(sm.buf + k_off(
+                                                                  wave, set, 16 * kb + p, 4 * kk + g)));
             float x[RT][2][4];
             float mloc[RT];
 #pragma unroll
@@ -398,6 +414,14 @@ struct Mfma {
                         x[rt][kb][i] = v;
                         mloc[rt] = fmaxf(mloc[rt], v);
                     }
+                }
+            }
+            if constexpr (KD) {
+                // K of this tile is consumed: the next tile's K streams now
+                gload_k(jn);
+                if constexpr (PAGED) {
+                    pg_cur[0] = pg_nxt[0];
+                    pg_cur[1] = pg_nxt[1];
                 }
             }
             // move the reference where a score passed it by more than kSlack
@@ -540,11 +564,11 @@ struct Mfma {
 // One workgroup per CU, one wave per SIMD: each wave keeps its head's rows
 // of accumulators and one K/V tile in registers.
 
-template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED, int POL, bool SMALL>
+template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED, int POL, bool SMALL, bool KD>
 __global__ __launch_bounds__(kMWaves * 64)
 __attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1, SMALL ? 2 : 1)))
 void split_kv_mfma_kernel(KernelArgs a) {
-    using M = Mfma<DT, DK, DV, HPW, PAGED, POL, SMALL>;
+    using M = Mfma<DT, DK, DV, HPW, PAGED, POL, SMALL, KD>;
     __shared__ __attribute__((aligned(16))) typename M::Smem sm;
     drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
                                  bool whole) {
@@ -552,14 +576,14 @@ void split_kv_mfma_kernel(KernelArgs a) {
     });
 }
 
-template <int DT, int DK, int DV, int HPW, int POL, bool SMALL = false>
+template <int DT, int DK, int DV, int HPW, int POL, bool SMALL = false, bool KD = false>
 const void *kernel_for(const KernelArgs &a) {
     const bool paged = a.block_table != nullptr;
     return a.schedule == kBalanced
-               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true, POL, SMALL>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false, POL, SMALL>)
-               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true, POL, SMALL>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false, POL, SMALL>);
+               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true, POL, SMALL, KD>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false, POL, SMALL, KD>)
+               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true, POL, SMALL, KD>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false, POL, SMALL, KD>);
 }
 
 template <int DT, int DK, int DV>
@@ -580,8 +604,9 @@ hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
     }
     // two kv heads per workgroup only with a single row block; several row
     // blocks re-read each head's K/V, which then keep the default cache policy
+    // and load K straight into the operand layout
     const void *fn = a.head_block == 2    ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY>(a)
-                     : a.row_blocks > 1 ? kernel_for<DT, DK, DV, 1, 0>(a)
+                     : a.row_blocks > 1 ? kernel_for<DT, DK, DV, 1, 0, false, true>(a)
                                         : kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY>(a);
     return hipLaunchKernel(fn, grid, dim3(kMWaves * 64), kargs, 0, stream);
 }

@@ -46,6 +46,10 @@ SHAPES = [
     ("valu_tokens64_r8", 2, 3, 4, 2, 64, 900, "fp16", True),
     ("mfma128", 2, 8, 16, 2, 128, 1100, "bf16", True),
     ("mfma64", 2, 2, 16, 1, 64, 1000, "fp16", False),
+    # several row blocks per kv head: K loaded straight into operand layout
+    ("mfma_rowblocks128", 2, 12, 16, 2, 128, 1000, "bf16", True),
+    ("mfma_rowblocks64", 2, 20, 8, 2, 64, 900, "fp16", False),
+    ("mfma_rowblocks256", 2, 4, 16, 2, 256, 700, "bf16", True),
 ]
 
 
