@@ -123,9 +123,9 @@ __device__ __forceinline__ float group_sum(float x) {
 // SMALL: one row tile (16 rows) per wave and one LDS stage, for at most 16
 // query rows per kv head; two workgroups share a CU.
 // KD: K is loaded from memory straight into the matrix operand layout (16
-// keys x 64 bytes per load instruction) instead of through LDS; used when
-// several row blocks of a head re-read its K/V from the caches, where the LDS
-// round trip, not the memory access pattern, is what limits the kernel.
+// keys x 64 bytes per load instruction) instead of through LDS (the 64-row
+// launches; it matters most when several row blocks of a head re-read its
+// K/V from the caches, where the LDS round trip limits the kernel).
 template <int DT, int DK, int DV, int HPW, bool PAGED, int POL = MXFA_KV_LOAD_POLICY,
           bool SMALL = false, bool KD = false>
 struct Mfma {
@@ -603,11 +603,12 @@ hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
         }
     }
     // two kv heads per workgroup only with a single row block; several row
-    // blocks re-read each head's K/V, which then keep the default cache policy
-    // and load K straight into the operand layout
-    const void *fn = a.head_block == 2    ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY>(a)
+    // blocks re-read each head's K/V, which then keep the default cache
+    // policy.  These launches load K straight into the operand layout (the
+    // 16-row variant above keeps the LDS path, which measured faster there).
+    const void *fn = a.head_block == 2    ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY, false, true>(a)
                      : a.row_blocks > 1 ? kernel_for<DT, DK, DV, 1, 0, false, true>(a)
-                                        : kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY>(a);
+                                        : kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY, false, true>(a);
     return hipLaunchKernel(fn, grid, dim3(kMWaves * 64), kargs, 0, stream);
 }
 
