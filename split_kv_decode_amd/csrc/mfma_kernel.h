@@ -27,8 +27,10 @@
 // Per tile, with v_mfma_f32_16x16x32 (lane l = 16 g + p; A: row p, k-slice
 // 8g..8g+7; B: k-slice 8g..8g+7, column p; C: rows 4g..4g+3, column p):
 //   S^T = K Q^T: A = 16 keys x 32 channels of K, loaded from memory straight
-//   into the operand layout (lane (g, p) loads 16 bytes of key p), B = Q^T
-//   (the lane's query row p of each row tile, resident in registers).  Lane
+//   into the operand layout (lane (g, p) loads 16 bytes of key p) in the
+//   64-row launches (KD), or read back from the wave's LDS tile (16-row
+//   variant), B = Q^T (the lane's query row p of each row tile, resident in
+//   registers).  Lane
 //   (g, p) receives the scores of keys 4g..4g+3 of each 16-key block for
 //   query row p, so every lane owns one query row per row tile: its running
 //   max m, running sum l and the rescale alpha are per lane (online softmax
@@ -41,8 +43,9 @@
 //   tile in LDS with two transposed reads (ds_read_b64_tr_b16: within a
 //   16-lane group, lane 4i + c reads 4 channels of key i and lane p receives
 //   channel p of the 4 keys).  One V^T operand serves all 4 row tiles.
-// V rows are stored in LDS with their 16-byte chunks XOR-swizzled by the key
-// index, so the keys read by one transposed read hit distinct banks.
+// V (and, without KD, K) rows are stored in LDS with their 16-byte chunks
+// XOR-swizzled by the key index, so the keys read by one transposed read hit
+// distinct banks.
 //
 // Paged caches.  With a block table, token j of sequence b is row j % page of
 // page block_table[b][j / page].  Tiles are then aligned to multiples of 32
