@@ -177,9 +177,12 @@ size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *fp) {
     constexpr int kChunkAlign = 64;
     constexpr int kTargetPerCU = 8;
-    // workgroups resident per CU: the VALU kernel runs two, the matrix-core
-    // kernel one (its LDS and registers fill the CU)
-    constexpr int kValuPerCU = 2;
+    // workgroups per CU in the balanced grid: one for the VALU kernel (it held
+    // two before; one measured 1-7% faster on MHA and GQA-2 decode batches of
+    // 0.5-2 GB and 0.5-0.7 us faster on the SmallQ calls, whose merge then
+    // reads half as many partials), two for the matrix-core kernel's 16-row
+    // variant, one for its 64-row tiles (their LDS and registers fill the CU)
+    constexpr int kValuPerCU = 1;
     constexpr int kMfmaPerCU = 1;
     mxfa_plan_t pl;
     std::memset(&pl, 0, sizeof(pl));

@@ -345,7 +345,7 @@ def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
     if p.schedule == 1:                      # balanced: planner's own choice only
         assert num_splits == 0 and p.combine == 1 and p.chunk == 0
         assert (p.grid_x, p.grid_y, p.grid_z) == (p.num_splits, 1, 1)
-        assert p.grid_x == p.num_cus * (2 if p.path == 0 or p.row_block == 16 else 1)
+        assert p.grid_x == p.num_cus * (2 if p.path == 1 and p.row_block == 16 else 1)
         assert p.workspace_bytes >= (p.num_splits + streams) * entry + (B + 2) * 8
         return
     S, C = p.num_splits, p.chunk
@@ -373,8 +373,12 @@ def test_balanced_schedule_is_chosen_for_long_ragged_batches():
 
 
 def test_balanced_grid_is_one_resident_wave_of_workgroups():
-    # VALU kernel: two workgroups per CU; matrix-core kernel: one per CU
-    assert m.plan(64, 32, 8, 128, 1, 16384, 0, 1, 0, 256).grid_x == 512
+    # matrix-core kernel: two workgroups per CU with 16-row tiles, else one;
+    # VALU kernel: one per CU
+    p = m.plan(64, 32, 8, 128, 1, 16384, 0, 1, 0, 256)
+    assert p.path == 1 and p.row_block == 16 and p.grid_x == 512
+    p = m.plan(64, 32, 32, 128, 1, 16384, 0, 1, 0, 256)
+    assert p.path == 0 and p.schedule == 1 and p.grid_x == 256
     p = m.plan(4, 64, 8, 128, 8, 32768, 1, 1, 0, 256)
     assert p.path == 1 and p.schedule == 1 and p.grid_x == 256
     assert m.plan(4, 64, 8, 128, 8, 32768, 1, 1, 0, 80).grid_x == 80
