@@ -194,7 +194,12 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     int hpb = 1;
     const bool valu_dims = p.dk() == p.dv() && (p.dk() == 64 || p.dk() == 128);
     const int mfma_min = p.dk() == 128 ? kMfmaMinRows128 : kMfmaMinRows;
-    if (R >= mfma_min || !valu_dims) {
+    // at exactly the 128-dim threshold, large caches stream faster through
+    // the VALU kernel (launch.h records the crossover)
+    const uint64_t cache_bytes =
+        (uint64_t)p.B * (uint64_t)p.kv_cap * p.Hkv * (uint64_t)(p.dk() + p.dv()) * 2;
+    const bool valu_stream = p.dk() == 128 && R == kMfmaMinRows128 && cache_bytes >= kValuStreamBytes;
+    if ((R >= mfma_min && !valu_stream) || !valu_dims) {
         // many rows per kv head (Q K^T and P V are dense 16-row tiles), or a
         // head shape only the matrix-core kernel's padded tiles hold
         pl.path = MXFA_PATH_MFMA;

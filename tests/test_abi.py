@@ -330,7 +330,9 @@ def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
     p = m.plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus)
     assert p.num_cus == (cus if cus > 0 else 256)
     assert p.rows == (Hq // Hkv) * qLen
-    if p.rows >= (4 if D == 128 else 8):
+    cache_bytes = B * cap * Hkv * D * 2 * 2
+    valu_stream = D == 128 and p.rows == 4 and cache_bytes >= 256 << 20
+    if p.rows >= (4 if D == 128 else 8) and not valu_stream:
         # matrix-core kernel: 16-row blocks up to 16 rows, else 64; two kv
         # heads per workgroup when Hkv is even and one block holds every row
         rb = 16 if p.rows <= 16 else 64
@@ -365,7 +367,7 @@ def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
 
 def test_balanced_schedule_is_chosen_for_long_ragged_batches():
     p = m.plan(64, 32, 8, 128, 1, 16384, 0, 1, 0, 256)
-    assert p.schedule == 1 and p.grid_x == 512
+    assert p.schedule == 1 and p.grid_x == 256
     p = m.plan(64, 32, 8, 128, 1, 16384, 0, 1, 16, 256)
     assert p.schedule == 0 and p.num_splits == 16
     p = m.plan(2000, 32, 8, 128, 1, 4096, 0, 1, 0, 256)     # batch past the LDS table
@@ -375,10 +377,21 @@ def test_balanced_schedule_is_chosen_for_long_ragged_batches():
 def test_balanced_grid_is_one_resident_wave_of_workgroups():
     # matrix-core kernel: two workgroups per CU with 16-row tiles, else one;
     # VALU kernel: one per CU
-    p = m.plan(64, 32, 8, 128, 1, 16384, 0, 1, 0, 256)
+    p = m.plan(2, 32, 8, 128, 1, 8192, 0, 1, 0, 256)
     assert p.path == 1 and p.row_block == 16 and p.grid_x == 512
     p = m.plan(64, 32, 32, 128, 1, 16384, 0, 1, 0, 256)
     assert p.path == 0 and p.schedule == 1 and p.grid_x == 256
+
+
+def test_four_rows_take_the_valu_kernel_on_large_caches():
+    # 4 rows per kv head at head dim 128: the 16-row matrix-core variant below
+    # 256 MiB of cache, the VALU kernel from there
+    small = m.plan(4, 32, 8, 128, 1, 8192, 0, 1)     # 134 MB
+    large = m.plan(8, 32, 8, 128, 1, 8192, 0, 1)     # 268 MB
+    assert small.path == 1 and small.row_block == 16
+    assert large.path == 0 and large.row_block == 4
+    assert m.plan(8, 32, 8, 64, 1, 16384, 0, 1).path == 0       # head dim 64: VALU below 8 rows
+    assert m.plan(8, 40, 8, 128, 1, 8192, 0, 1).path == 1       # 5 rows: matrix core
     p = m.plan(4, 64, 8, 128, 8, 32768, 1, 1, 0, 256)
     assert p.path == 1 and p.schedule == 1 and p.grid_x == 256
     assert m.plan(4, 64, 8, 128, 8, 32768, 1, 1, 0, 80).grid_x == 80
