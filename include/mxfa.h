@@ -88,8 +88,8 @@ typedef enum { MXFA_FP16 = 0, MXFA_BF16 = 1 } mxfa_dtype;
 typedef enum {
     MXFA_PATH_VALU = 0,         /* vector-ALU split kernel (few rows per kv head) */
     MXFA_PATH_MFMA = 1          /* matrix-core split kernel (>= 4 rows per kv head at head dim 128, or >= 5
-                                   when the caches hold 256 MiB or more; >= 8 at 64; head dims other
-                                   than 64 / 128) */
+                                   when contiguous caches hold 256 MiB or more; >= 8 at 64; head dims
+                                   other than 64 / 128) */
 } mxfa_path;
 
 /* How a call is carried out.  The analogue of the dispatch record the

@@ -177,14 +177,15 @@ hipError_t launch_append(const KernelArgs &a, const void *k_new, const void *v_n
 // ahead (189 against 199 us), and at 1-2 rows the two trade places by case.
 constexpr int kMfmaMinRows = 8;
 constexpr int kMfmaMinRows128 = 4;
-// ... except at exactly 4 rows (head dim 128) when the caches hold at least
-// this many bytes (B * kv_cap * Hkv * (Dk + Dv) * 2): after the VALU kernel
+// ... except at exactly 4 rows (head dim 128) when contiguous caches hold at
+// least this many bytes (B * kv_cap * Hkv * (Dk + Dv) * 2): after the VALU kernel
 // moved to one workgroup per CU it streamed such batches faster than the
 // 16-row variant, which ramps up faster on small ones.  Measured per call
 // (GQA 4, head dim 128, 8192 keys): 67 MB 18.4 (matrix core) against 21.8 us
 // (VALU), 134 MB 29.3 against 30.3, 268 MB 51.3 against 49.3, 537 MB 88.3
 // against 86.7; Qwen3-8B 345.5 against 340.7, Qwen3-4B long 159.7 against
-// 158.8.
+// 158.8.  Paged caches keep the matrix-core kernel: through 16-256 token
+// pages the VALU kernel took 434 against 351 us on the Qwen3-8B batch.
 constexpr unsigned long long kValuStreamBytes = 256ull << 20;
 // At most 16 rows per kv head (e.g. GQA 8 with one query token): the
 // matrix-core kernel's small variant, one 16-row tile per wave and two
