@@ -147,8 +147,8 @@ int valu_layout(int Hkv, int D, int *heads_per_block) {
 //   full length, but no shorter than a floor that keeps the partial results
 //   (row_block x (D + 1) floats per head, written once, read once by the
 //   merge) a small fraction of the partition's K/V bytes.
-//   Balanced: a fixed grid of as many workgroups as are resident at once
-//   (two per CU for the VALU kernel, one for the matrix-core kernel), each taking
+//   Balanced: a fixed grid of one or two workgroups per CU (see make_plan),
+//   each taking
 //   an equal share (at least the same floor) of all streams laid end to end,
 //   so ragged batches keep every workgroup equally busy.
 // The balanced schedule is used when the planner is free to choose
