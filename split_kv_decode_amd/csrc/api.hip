@@ -234,12 +234,13 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     const int rows_held = (int)(R < pl.row_block ? R : pl.row_block);
     const int min_chunk =
         ceil_div(16 * rows_held > 64 ? 16 * rows_held : 64, kChunkAlign) * kChunkAlign;
-    // the balanced share floor: the same rule down to 32 tokens (1 or 2 rows
-    // per kv head).  Measured on the 1023-token SmallQ cases, where the floor
-    // decides how many workgroups get work: 14.3 against 17.4 us per call at
-    // q1, 15.8 against 18.7 at q2; 16 tokens gained nothing more.
+    // the balanced share floor: 8 tokens per row held, at least 32.  Measured
+    // on the 1023-token SmallQ cases, where the floor decides how many
+    // workgroups get work: 14.3 against 17.4 us per call at q1 and 15.8
+    // against 18.7 at q2 for 32 tokens against 64 (16 gained nothing more),
+    // and 16.3 against 16.7 us at q8 for 64 tokens against 128.
     constexpr int kShareAlign = 32;
-    const int min_share = ceil_div(16 * rows_held > 32 ? 16 * rows_held : 32, kShareAlign) *
+    const int min_share = ceil_div(8 * rows_held > 32 ? 8 * rows_held : 32, kShareAlign) *
                           kShareAlign;
 
     int S, chunk;
