@@ -44,8 +44,8 @@
 //   16-lane group, lane 4i + c reads 4 channels of key i and lane p receives
 //   channel p of the 4 keys).  One V^T operand serves all 4 row tiles.
 // V (and, without KD, K) rows are stored in LDS with their 16-byte chunks
-// XOR-swizzled by the key index, so the keys read by one transposed read hit
-// distinct banks.
+// XOR-swizzled by the key index (twice the key index for V), so the keys read
+// by one transposed read hit distinct banks.
 //
 // Paged caches.  With a block table, token j of sequence b is row j % page of
 // page block_table[b][j / page].  Tiles are then aligned to multiples of 32
@@ -149,7 +149,11 @@ struct Mfma {
     static constexpr int RB = RT * 16;            // query rows per workgroup and head
     static constexpr int WPH = kMWaves / HPW;     // waves per kv head
     // XOR swizzle of the 16-byte chunks of a row by the key index, within
-    // aligned groups of SW chunks (a power of two)
+    // aligned groups of SW chunks (a power of two).  V rows use twice the key
+    // index: a transposed read takes 2 chunks of 4 consecutive keys, which
+    // then land in 8 distinct chunk slots (with the plain key index keys 2i
+    // and 2i + 1 swap the same two slots, a 2-way bank conflict when rows
+    // are a multiple of 256 bytes)
     static constexpr int SWK = (NCHK & (NCHK - 1)) == 0 ? NCHK : 8;
     static constexpr int SWV = (NCHV & (NCHV - 1)) == 0 ? NCHV : 8;
     static_assert(DK % 32 == 0 && DV % 32 == 0 && DK <= 256 && DV <= 256, "tile widths");
@@ -177,7 +181,7 @@ struct Mfma {
     }
     __device__ static uint32_t v_off(int wave, int stage, int key, int chunk) {
         return (uint32_t)((wave * STG + stage) * (KTB + VTB) + KTB + key * ROWV +
-                          ((chunk ^ (key % SWV)) * 16));
+                          ((chunk ^ ((2 * key) % SWV)) * 16));
     }
     __device__ static uint32_t o_off(int src, int row, int ch) {
         return (uint32_t)((src * RB + row) * ORS + ch * 4);
