@@ -14,7 +14,7 @@ Hkv=8, D=128, bf16, KV cache of 16384 with per-sequence lengths uniform in
   roofline   the split kernel alone: its algorithmic bytes (K/V rows + Q) per
              launch / its mean duration from HIP events recorded around it on
              the stream it runs on, against the 8 TB/s HBM peak; traffic from
-             a committed rocprofv3 counter summary when it matches this build;
+             a committed rocprofv3 counter summary when it matches the current kernel sources;
   cpu_baseline  the fp64 CPU oracle timed on this host on the same inputs
              (median of up to 3 runs with every core it may use, and a
              one-thread figure on a sample of the batch);
@@ -296,8 +296,8 @@ def main():
         summarize_profiles(*args.summarize_profiles, args.workload, args.profile_command)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the split-KV path shards by batch or kv head with no exchange; see DESIGN.md)",
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the split-KV path shards by batch or kv head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
