@@ -50,6 +50,7 @@ SHAPES = [
     ("mfma_rowblocks128", 2, 12, 16, 2, 128, 1000, "bf16", True),
     ("mfma_rowblocks64", 2, 20, 8, 2, 64, 900, "fp16", False),
     ("mfma_rowblocks256", 2, 4, 16, 2, 256, 700, "bf16", True),
+    ("mfma128_oddkv", 2, 8, 24, 3, 128, 900, "bf16", True),    # 64 rows, one head per workgroup
 ]
 
 

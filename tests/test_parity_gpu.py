@@ -148,6 +148,19 @@ def test_matrix_core_many_rows_keep_one_head_per_workgroup():
     assert plan["path"] == "mfma" and plan["head_block"] == 1 and plan["rows"] == 160
 
 
+@pytest.mark.parametrize("Hkv,qLen", [(3, 8), (3, 5), (5, 6)])
+def test_matrix_core_one_block_one_head(Hkv, qLen):
+    """One 64-row block per kv head with an odd Hkv: one kv head per
+    workgroup, K loaded straight into the operand layout, ragged lengths and
+    a causal draft."""
+    w = wl.Workload("onehead", B=3, qLen=qLen, Hq=8 * Hkv, Hkv=Hkv, D=128, kv_cap=800,
+                    dtype="bf16", causal=True, sigma=1.0, seed=960 + Hkv + qLen,
+                    len_range=(1, 800))
+    inp = wl.make_inputs(w, lengths=[800, 217, 3])
+    _, _, plan = _full_check(inp)
+    assert plan["path"] == "mfma" and plan["head_block"] == 1 and plan["row_block"] == 64
+
+
 @pytest.mark.parametrize("kvlen", [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 1025])
 def test_kv_length_sweep(kvlen):
     w = wl.Workload("lens", B=1, qLen=1, Hq=4, Hkv=1, D=128, kv_cap=kvlen, dtype="fp16",
