@@ -130,14 +130,20 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
     } else {
         __shared__ long long cum[kMaxBalancedBatch + 1];
         __shared__ long long wave_tot[kScheduleThreads / 64];
-        length_prefix_sums(a, cum, wave_tot);
-        const long long T = uni(cum[a.B] * HR);
+        // Without per-sequence lengths every sequence holds the same number
+        // of keys, so the prefix sums are b * n and no workgroup waits for
+        // the length loads and the scan before requesting its first tile.
+        const bool uniform = a.seqlens == nullptr && a.cu_k == nullptr;
+        const long long n_u = uniform ? seq_len_from(a, 0, 0) : 0;
+        if (!uniform) length_prefix_sums(a, cum, wave_tot);
+        auto cumv = [&](int bb) -> long long { return uniform ? bb * n_u : cum[bb]; };
+        const long long T = uni(cumv(a.B) * HR);
         long long W = div_nn(T + a.S - 1, a.S);
         if (W < a.min_share) W = a.min_share;
         W = uni(W);
         if (blockIdx.x == 0) {
             for (int bb = threadIdx.x; bb <= a.B; bb += kScheduleThreads)
-                ((long long *)a.ws_cum)[bb] = cum[bb];
+                ((long long *)a.ws_cum)[bb] = cumv(bb);
             if (threadIdx.x == 0) ((long long *)a.ws_cum)[a.B + 1] = W;
         }
         // shares with work: fewer than the grid when W is held up by min_share
@@ -148,14 +154,19 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         if (g >= T) return;
         const long long gend = g + W < T ? g + W : T;
         // sequence holding global token g: the last b with cum[b] * HR <= g
+        // (g < T, so with uniform lengths n_u > 0)
         int lo = 0, hi = a.B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cum[mid] * HR <= g) lo = mid; else hi = mid - 1;
+        if (uniform) {
+            lo = (int)div_nn(g, n_u * HR);
+        } else {
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (cum[mid] * HR <= g) lo = mid; else hi = mid - 1;
+            }
         }
         int b = uni(lo);
-        int n = uni((int)(cum[b + 1] - cum[b]));
-        const long long off = uni(g - cum[b] * HR);
+        int n = uni((int)(cumv(b + 1) - cumv(b)));
+        const long long off = uni(g - cumv(b) * HR);
         int j = uni((int)div_nn(off, n));
         int t = uni((int)(off - (long long)j * n));
         while (g < gend) {
@@ -166,10 +177,10 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
             t = 0;
             if (++j == HR) {
                 j = 0;
-                do { ++b; } while (b < a.B && cum[b + 1] == cum[b]);
+                do { ++b; } while (b < a.B && cumv(b + 1) == cumv(b));
                 b = uni(b);
                 if (b >= a.B) break;
-                n = uni((int)(cum[b + 1] - cum[b]));
+                n = uni((int)(cumv(b + 1) - cumv(b)));
             }
         }
     }
