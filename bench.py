@@ -19,7 +19,16 @@ Hkv=8, D=128, bf16, KV cache of 16384 with per-sequence lengths uniform in
              (median of up to 3 runs with every core it may use, and a
              one-thread figure on a sample of the batch);
   read_ceiling  the library's streaming-read probe over 2 GiB (nt and default
-             cache policy): the practical HBM read rate on this GPU.
+             cache policy): the practical HBM read rate on this GPU;
+  mfma_util  for the matrix-core path: attention flops (4 D per visible
+             (row, key) pair) per split-kernel launch and per call against the
+             2.5 PFLOP/s dense bf16/fp16 peak;
+  dispatch_check  a few calls under the profiler must have dispatched
+             exactly one split kernel each, plus one merge kernel when the
+             plan has a merge, and nothing else (the run fails otherwise);
+  configs    the same figures for every other named decode workload (the
+             tiny causal case, the 12 SmallQ cases, the Qwen3-4B and
+             Llama-70B batches), each over its own 1000 timed calls.
 
 Caches smaller than 1 GiB are timed over rotating copies (enough that the
 copies together hold at least 1 GiB of K/V, at most 64), so that no call
@@ -40,34 +49,41 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "qwen3_8b_decode"
-KERNEL_SOURCES = ["split_kv_decode_amd/csrc/split_valu.hip",
-                  "split_kv_decode_amd/csrc/split_mfma.hip",
-                  "split_kv_decode_amd/csrc/split_mfma_wide.hip",
-                  "split_kv_decode_amd/csrc/mfma_kernel.h",
-                  "split_kv_decode_amd/csrc/schedule.h",
-                  "split_kv_decode_amd/csrc/device_common.h",
-                  "split_kv_decode_amd/csrc/launch.h"]
+# the sources each split kernel is compiled from, plus the planner that
+# chooses its launch (grid, partial results): a counter record is valid only
+# while none of them has changed
+_COMMON = ["split_kv_decode_amd/csrc/schedule.h", "split_kv_decode_amd/csrc/device_common.h",
+           "split_kv_decode_amd/csrc/launch.h", "split_kv_decode_amd/csrc/api.hip",
+           "include/mxfa.h"]
+KERNEL_SOURCES = {
+    "split_kv_valu_kernel": ["split_kv_decode_amd/csrc/split_valu.hip"] + _COMMON,
+    "split_kv_mfma_kernel": ["split_kv_decode_amd/csrc/split_mfma.hip",
+                             "split_kv_decode_amd/csrc/split_mfma_wide.hip",
+                             "split_kv_decode_amd/csrc/mfma_kernel.h"] + _COMMON,
+}
 SPLIT_KERNEL = {"valu": "split_kv_valu_kernel", "mfma": "split_kv_mfma_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_digest() -> str:
+def kernel_digest(kernel: str) -> str:
+    """Digest of the sources `kernel` is built and planned from."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str):
+def traffic_for(workload: str, kernel: str):
     """HBM bytes per split-kernel launch from the committed counter summary,
-    or None when there is none for this workload or the kernel changed."""
+    or None when there is none for this workload and kernel, or when the
+    kernel's sources changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_digest") != kernel_digest():
+    if not rec or rec.get("kernel") != kernel or rec.get("kernel_digest") != kernel_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -105,8 +121,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands):
     f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
     split = [k for k in f_by if "split_kv_" in k][0]
     merge = [k for k in f_by if "combine_kernel" in k]
-    f_split = statistics.median(f_by[split]) * f_scale
-    w_split = statistics.median(w_by[split]) * w_scale
+    f_raw, w_raw = statistics.median(f_by[split]), statistics.median(w_by[split])
+    f_split, w_split = f_raw * f_scale, w_raw * w_scale
 
     import workloads as wl
     w = wl.WORKLOADS[workload]
@@ -129,16 +145,20 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands):
               f"- copy calibration: a 1 GiB device copy reads as {f_copy / 2**20:.1f} MiB of "
               f"FETCH_SIZE and {w_copy / 2**20:.1f} MiB of WRITE_SIZE; scale factors "
               f"{f_scale:.3f} (fetch) and {w_scale:.3f} (write)",
-              f"- split kernel: fetch {f_split / 1e9:.4f} GB, write {w_split / 1e9:.4f} GB "
-              f"(scaled medians over {len(f_by[split])} launches)",
+              f"- split kernel, raw counters (medians over {len(f_by[split])} launches): "
+              f"FETCH_SIZE {f_raw / 1024:.0f} KiB ({f_raw / 1e9:.4f} GB), WRITE_SIZE "
+              f"{w_raw / 1024:.0f} KiB ({w_raw / 1e9:.4f} GB) per launch",
+              f"- split kernel, scaled: fetch {f_split / 1e9:.4f} GB (x{f_scale:.3f}), write "
+              f"{w_split / 1e9:.4f} GB (x{w_scale:.3f})",
               f"- algorithmic bytes per launch (K/V rows read once + Q): {alg / 1e9:.4f} GB; "
               f"fetched / algorithmic = {f_split / alg:.4f}",
               f"- achieved from the trace average: {alg / (avg_ns * 1e-9) / 1e9:.1f} GB/s "
               f"({100 * alg / (avg_ns * 1e-9) / 1e9 / HBM_PEAK_GBS:.1f}% of 8 TB/s)"]
     if merge:
-        fm = statistics.median(f_by[merge[0]]) * f_scale
-        wm = statistics.median(w_by[merge[0]]) * w_scale
-        lines.append(f"- merge kernel: fetch {fm / 1e6:.2f} MB, write {wm / 1e6:.2f} MB per launch")
+        fmr, wmr = statistics.median(f_by[merge[0]]), statistics.median(w_by[merge[0]])
+        lines.append(f"- merge kernel: raw FETCH_SIZE {fmr / 1024:.0f} KiB, WRITE_SIZE "
+                     f"{wmr / 1024:.0f} KiB; scaled fetch {fmr * f_scale / 1e6:.2f} MB, write "
+                     f"{wmr * w_scale / 1e6:.2f} MB per launch")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     path = os.path.join(ROOT, "profiles", f"{kname}_{workload}.md")
     with open(path, "w") as f:
@@ -148,9 +168,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands):
             rec = json.load(f)
     except (OSError, ValueError):
         rec = {}
-    rec[workload] = {"kernel": kname, "kernel_digest": kernel_digest(),
+    rec[workload] = {"kernel": kname, "kernel_digest": kernel_digest(kname),
                      "bytes_per_launch": int(round(f_split + w_split)),
                      "fetch_bytes": int(round(f_split)), "write_bytes": int(round(w_split)),
+                     "fetch_raw_kib": round(f_raw / 1024, 1), "write_raw_kib": round(w_raw / 1024, 1),
                      "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -281,6 +302,12 @@ def parse():
                     help="rotating copies of the inputs (0 = enough for 1 GiB of K/V, <= 64)")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the 2 GiB streaming-read probe")
+    ap.add_argument("--no-dispatch-check", action="store_true",
+                    help="skip the profiler count of the kernels each call dispatches "
+                         "(for runs under an external profiler)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the chosen workload (by default the other named "
+                         "decode workloads are measured too and summarised under 'configs')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"),
@@ -312,10 +339,82 @@ def main():
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    m = measure_decode(w, args.steps, args.warmup, args.page_size, args.num_splits,
+                       args.copies, torch, np, mx, wl, dev, not args.no_dispatch_check)
+    ceiling = (read_ceiling(torch, mx, dev, m["stream"], m["kv"])
+               if not args.no_read_ceiling else None)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    P = args.page_size
+    traffic = traffic_for(f"{w.name}_paged{P}" if P else w.name, m["kernel"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, w, m["inp"], m["paged_cpu"], m["lens"], m["alg_bytes"])
+    configs = None
+    if not args.no_configs and not P and args.num_splits == 0:
+        del m["inp"], m["paged_cpu"]
+        configs = other_configs(w.name, args, torch, np, mx, wl, dev)
+    split_gbs = m["split_gbs"]
+    rec = {
+        "metric": "decode attention achieved HBM GB/s (% of peak) and attn-calls/s at B x KV len",
+        "value": round(m["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "qLen": w.qLen, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "D": w.D, "kv_cap": w.kv_cap, "sum_kv_len": int(sum(m["lens"])),
+                   "causal": w.causal, "kv_layout": f"paged{P}" if P else "contiguous",
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * m["gbs"] / HBM_PEAK_GBS, 2),
+        # one over the median event-timed call (split + merge kernels)
+        "attn_calls_per_s": round(1e3 / m["call_ms_median"], 1),
+        "median_call_us": round(m["call_ms_median"] * 1e3, 2),
+        "wall_calls_per_s": round(1e3 / m["ms_per_step"], 1),
+        "rotating_copies": m["n_copies"],
+        "plan": m["plan"],
+        "dispatch_check": m["dispatch"],
+        "roofline": {"bound": "hbm", "kernel": m["kernel"],
+                     "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "bytes_per_launch": m["split_bytes"],
+                     "mean_launch_us": round(m["split_ms_mean"] * 1e3, 2),
+                     "median_launch_us": round(m["split_ms_median"] * 1e3, 2),
+                     "frac_of_read_ceiling": (round(split_gbs / ceiling["nt_gbs"], 4)
+                                              if ceiling else None),
+                     "frac_of_size_matched_ceiling": (
+                         round(split_gbs / ceiling["nt_gbs_at_workload_size"], 4)
+                         if ceiling and "nt_gbs_at_workload_size" in ceiling else None)},
+        "mfma_util": m["mfma_util"],
+        "read_ceiling": ceiling,
+        "cpu_baseline": cpu,
+        "configs": configs,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def measure_decode(w, steps, warmup, page_size, num_splits, copies, torch, np, mx, wl, dev,
+                   dispatch_check=True):
+    """Time one decode workload: exactly `steps` whole calls (after `warmup`)
+    by the wall clock, the split kernel alone by HIP events recorded around it
+    on its stream, and whole calls between event pairs; check the dispatch
+    count of a few calls in a profiler trace.  Returns a dict of figures."""
     t0 = time.time()
     inp = wl.make_inputs(w)
     lens = inp.lengths()
-    P = args.page_size
+    P = page_size
     paged_cpu = wl.to_paged(inp, P) if P else None
     paged = paged_cpu.to(dev) if P else None
     g = inp.to(dev) if not P else None
@@ -326,18 +425,17 @@ def main():
     dt = mx.MXFA_BF16 if w.dtype == "bf16" else mx.MXFA_FP16
     if P:
         need = mx.workspace_size_paged(w.B, w.Hq, w.Hkv, w.D, w.qLen, P,
-                                       paged.block_table.shape[1], w.causal, dt,
-                                       args.num_splits)
+                                       paged.block_table.shape[1], w.causal, dt, num_splits)
     else:
         need = mx.workspace_size(w.B, w.Hq, w.Hkv, w.D, w.qLen, w.kv_cap, w.causal, dt,
-                                 args.num_splits)
+                                 num_splits)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     # rotating copies of q / K / V / out / lse (the block table and the
     # lengths are shared)
     kv = wl.kv_bytes(w, lens)
-    n_copies = (args.copies if args.copies > 0
+    n_copies = (copies if copies > 0
                 else max(1, min(MAX_COPIES, -(-ROTATE_BYTES // max(kv, 1)))))
     k0, v0 = (paged.k_pages, paged.v_pages) if P else (g.k_cache, g.v_cache)
     sets = []
@@ -350,12 +448,12 @@ def main():
     # enqueues the next copy's call
     if P:
         calls = [mx.fwd_kvcache_paged(qc, kc, vc, paged.block_table, paged.cache_seqlens,
-                                      w.causal, out=oc, lse=lc, num_splits=args.num_splits,
+                                      w.causal, out=oc, lse=lc, num_splits=num_splits,
                                       workspace=ws, stream=stream.cuda_stream, prepare=True)
                  for qc, kc, vc, oc, lc in sets]
     else:
         calls = [mx.fwd_kvcache(qc, kc, vc, g.cache_seqlens, w.causal, out=oc, lse=lc,
-                                num_splits=args.num_splits, workspace=ws,
+                                num_splits=num_splits, workspace=ws,
                                 stream=stream.cuda_stream, prepare=True)
                  for qc, kc, vc, oc, lc in sets]
     counter = [0]
@@ -364,22 +462,21 @@ def main():
         calls[counter[0] % n_copies].run()
         counter[0] += 1
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         call()
     torch.cuda.synchronize()
     plan = mx.last_plan().as_dict()
 
-    # whole calls, wall clock over exactly K steps
+    # whole calls, wall clock over exactly `steps` calls
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         call()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / steps
 
     new_events = lambda: [(torch.cuda.Event(enable_timing=True),
-                           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+                           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     # split kernel alone: HIP events recorded around it on its stream
     evs = new_events()
     for a, b in evs:          # create the underlying HIP events
@@ -401,17 +498,8 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     call_ms_median = statistics.median(a.elapsed_time(b) for a, b in cevs)
-
-    ceiling = (read_ceiling(torch, mx, dev, stream, kv) if not args.no_read_ceiling
-               else None)
-
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    dispatch = (check_dispatch(call, plan, torch) if dispatch_check
+                else {"checked": False, "reason": "--no-dispatch-check"})
 
     alg_bytes = wl.algorithmic_bytes(w, lens)
     q_bytes = w.B * w.qLen * w.Hq * w.D * w.elt
@@ -419,54 +507,98 @@ def main():
     bt_bytes = sum(-(-max(0, min(n, w.kv_cap)) // P) for n in lens) * 4 if P else 0
     alg_bytes += bt_bytes
     split_bytes = kv + q_bytes + bt_bytes
-    gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
-    split_gbs = split_bytes / (split_ms_mean * 1e-3) / 1e9
-    traffic = traffic_for(f"{w.name}_paged{P}" if P else w.name)
+    flops = wl.flops(w, lens)
+    mfma_util = None
+    if plan["path"] == "mfma":
+        # attention flops (4 D per visible (row, key) pair) against the dense
+        # matrix-core peak of the input type
+        mfma_util = {"flops_per_call": flops,
+                     "split_tflops": round(flops / (split_ms_mean * 1e-3) / 1e12, 2),
+                     "split_frac_of_peak": round(flops / (split_ms_mean * 1e-3) / 1e12
+                                                 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "call_frac_of_peak": round(flops / (ms_per_step * 1e-3) / 1e12
+                                                / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+    kernel = SPLIT_KERNEL[plan["path"]]
+    out = {"inp": inp, "paged_cpu": paged_cpu, "lens": lens, "kv": kv, "stream": stream,
+           "plan": plan, "kernel": kernel, "n_copies": n_copies,
+           "ms_per_step": ms_per_step, "split_ms_mean": split_ms_mean,
+           "split_ms_median": statistics.median(split_ms), "call_ms_median": call_ms_median,
+           "alg_bytes": alg_bytes, "split_bytes": split_bytes,
+           "gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+           "split_gbs": split_bytes / (split_ms_mean * 1e-3) / 1e9,
+           "mfma_util": mfma_util, "dispatch": dispatch}
+    del calls, sets, ws, g, paged, q
+    return out
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, w, inp, paged_cpu, lens, alg_bytes)
 
-    rec = {
-        "metric": "decode attention achieved HBM GB/s (% of peak) and attn-calls/s at B x KV len",
-        "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "qLen": w.qLen, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "D": w.D, "kv_cap": w.kv_cap, "sum_kv_len": int(sum(lens)),
-                   "causal": w.causal, "kv_layout": f"paged{P}" if P else "contiguous",
-                   "parallelism": "single GPU"},
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        # one over the median event-timed call (split + merge kernels)
-        "attn_calls_per_s": round(1e3 / call_ms_median, 1),
-        "median_call_us": round(call_ms_median * 1e3, 2),
-        "wall_calls_per_s": round(1e3 / ms_per_step, 1),
-        "rotating_copies": n_copies,
-        "plan": plan,
-        "roofline": {"bound": "hbm", "kernel": SPLIT_KERNEL[plan["path"]],
-                     "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(split_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "bytes_per_launch": split_bytes,
-                     "mean_launch_us": round(split_ms_mean * 1e3, 2),
-                     "median_launch_us": round(statistics.median(split_ms) * 1e3, 2),
-                     "frac_of_read_ceiling": (round(split_gbs / ceiling["nt_gbs"], 4)
-                                              if ceiling else None),
-                     "frac_of_size_matched_ceiling": (
-                         round(split_gbs / ceiling["nt_gbs_at_workload_size"], 4)
-                         if ceiling and "nt_gbs_at_workload_size" in ceiling else None)},
-        "read_ceiling": ceiling,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(rec), flush=True)
+DISPATCH_CALLS = 4
+
+
+def check_dispatch(call, plan, torch):
+    """Enqueue DISPATCH_CALLS calls under the profiler and count the kernels
+    the GPU ran: each call must dispatch exactly one split kernel, plus one
+    merge kernel when the plan has a merge, and nothing else.  Raises on a
+    mismatch; returns the counts.  Without device events in the trace (no
+    kernel tracing on this system) the check is reported as not run."""
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for _ in range(DISPATCH_CALLS):
+            call()
+        torch.cuda.synchronize()
+    counts = {}
+    for e in prof.events():
+        dt = str(getattr(e, "device_type", ""))
+        if "CUDA" in dt or "HIP" in dt:
+            counts[e.name] = counts.get(e.name, 0) + 1
+    if not counts:
+        return {"checked": False, "reason": "the profiler recorded no device kernels"}
+    split = sum(c for n, c in counts.items() if "split_kv_" in n)
+    merge = sum(c for n, c in counts.items() if "combine_kernel" in n)
+    other = sum(counts.values()) - split - merge
+    want_merge = DISPATCH_CALLS if plan["combine"] else 0
+    ok = split == DISPATCH_CALLS and merge == want_merge and other == 0
+    rec = {"checked": True, "calls": DISPATCH_CALLS, "split_launches": split,
+           "merge_launches": merge, "other_kernels": other, "ok": ok}
+    if not ok:
+        raise RuntimeError(f"dispatch check failed: {rec}; kernels {counts}")
+    return rec
+
+
+CONFIG_STEPS, CONFIG_WARMUP = 1000, 50
+
+
+def other_configs(headline, args, torch, np, mx, wl, dev):
+    """Every other named decode workload, each measured like the headline
+    (its own CONFIG_STEPS calls after CONFIG_WARMUP, rotating copies, event
+    timings, dispatch check) and summarised in one record."""
+    recs = []
+    for name, w in wl.WORKLOADS.items():
+        if name == headline:
+            continue
+        m = measure_decode(w, CONFIG_STEPS, CONFIG_WARMUP, 0, 0, 0, torch, np, mx, wl, dev,
+                           not args.no_dispatch_check)
+        gbs = m["gbs"]
+        recs.append({
+            "workload": name, "B": w.B, "qLen": w.qLen, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+            "kv_cap": w.kv_cap, "sum_kv_len": int(sum(m["lens"])), "dtype": w.dtype,
+            "causal": w.causal, "steps": CONFIG_STEPS, "warmup": CONFIG_WARMUP,
+            "wall_us_per_call": round(m["ms_per_step"] * 1e3, 2),
+            "median_call_us": round(m["call_ms_median"] * 1e3, 2),
+            "gb_per_s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "attn_calls_per_s": round(1e3 / m["call_ms_median"], 1),
+            "rotating_copies": m["n_copies"],
+            "path": m["plan"]["path"], "combine": m["plan"]["combine"],
+            "split": {"kernel": m["kernel"], "mean_launch_us": round(m["split_ms_mean"] * 1e3, 2),
+                      "gb_per_s": round(m["split_gbs"], 1),
+                      "frac": round(m["split_gbs"] / HBM_PEAK_GBS, 4)},
+            "mfma_util": m["mfma_util"], "dispatch_check": m["dispatch"]})
+        print(f"# {name}: {recs[-1]['wall_us_per_call']} us/call, "
+              f"{recs[-1]['pct_of_hbm_peak']}% of peak", file=sys.stderr, flush=True)
+        del m
+        torch.cuda.empty_cache()
+    return recs
 
 
 ROTATE_BYTES = 1 << 30

@@ -50,8 +50,11 @@
  * mxfa_set_timing_events) and a per-device cache of the CU count, so calls
  * from several host threads are safe.
  *
- * Asynchrony: kernels are enqueued on `stream` (a hipStream_t; NULL = the
- * null stream) and the call returns without synchronising.  The status
+ * Asynchrony: kernels are enqueued on `stream` (a hipStream_t passed as
+ * void *, so that this header needs no HIP header and plain C and ctypes
+ * callers can use it; NULL = the null stream) and the call returns without
+ * synchronising, as in the SmallQ FlashAttention README's "aclnn API call"
+ * section, where the caller synchronises the stream.  The status
  * covers argument checks and launch errors only; faults during execution
  * surface at the caller's next synchronisation.
  *
@@ -116,7 +119,13 @@ typedef struct {
     size_t workspace_bytes;      /* device scratch the call needs (0 without merge) */
 } mxfa_plan_t;
 
-/* Split-KV decode attention, library-managed scratch.
+/* Split-KV decode attention, library-managed scratch: the FlashAttention-
+ * compatible attention-with-KV-cache entry point of the MXFlashAttn package
+ * page (Python API section), computed by the split-KV decode method its
+ * use-case section describes.  The arguments carry what the Python API keeps
+ * in tensor shapes, so the cache capacity kv_cap (the cache's second
+ * dimension) is passed explicitly: without it the batch stride of a
+ * contiguous [B, kv_cap, Hkv, D] cache is unknown.
  * Partial results of the KV partitions go to a scratch buffer taken from
  * the stream-ordered allocator (hipMallocAsync / hipFreeAsync on `stream`).
  * Arguments as in the conventions above.  causal is 0 or 1; dtype is an
@@ -131,7 +140,10 @@ MXFA_API mxfa_status mxfa_fwd_kvcache(const void *q, const void *k_cache,
                                       int dtype, void *stream);
 
 /* Same computation with caller-provided scratch and an optional forced
- * partition count.  num_splits = 0 lets the planner choose; a positive value
+ * partition count: the execute half of the two-phase call of the SmallQ
+ * FlashAttention README's "aclnn API call" section (query the workspace size,
+ * allocate it, then enqueue the operator on a stream and let the caller
+ * synchronise).  num_splits = 0 lets the planner choose; a positive value
  * asks for that many KV partitions per (batch, kv head) at kv_cap (clamped to
  * [1, kv_cap]).  workspace must be 256-byte aligned and hold at least the
  * number of bytes mxfa_workspace_size reports for the same arguments; it may
@@ -148,7 +160,12 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_ws(const void *q, const void *k_cache,
                                          size_t workspace_bytes, void *stream);
 
 /* Scratch bytes that mxfa_fwd_kvcache_ws needs for these arguments, written
- * to *bytes.  The partitioning depends on the CU count of the current HIP
+ * to *bytes: the size-query half of the two-phase call of the SmallQ
+ * FlashAttention README's "aclnn API call" section, which likewise writes the
+ * size through a pointer and returns a status.  It takes the execute call's
+ * problem arguments (causal and dtype included) and checks them the same
+ * way, so a bad problem is reported before any allocation.  The
+ * partitioning depends on the CU count of the current HIP
  * device, so call it with the device current that will run the attention
  * (the count is queried once per device and cached).  Returns the same
  * validation statuses as the attention calls (checked before any HIP call),
@@ -200,7 +217,9 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_paged_ws(
     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Scratch bytes that mxfa_fwd_kvcache_paged_ws needs (the pool size does not
- * enter); same validation and device rules as mxfa_workspace_size. */
+ * enter); the size query of the two-phase call (SmallQ FlashAttention README,
+ * "aclnn API call"), with the validation and device rules of
+ * mxfa_workspace_size. */
 MXFA_API mxfa_status mxfa_workspace_size_paged(int B, int Hq, int Hkv, int D,
                                                int qLen, int page_size,
                                                int max_pages, int causal,
@@ -288,25 +307,36 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_dkdv(const void *q, const void *k_cache,
                                            int num_splits, void *workspace,
                                            size_t workspace_bytes, void *stream);
 
-/* Scratch bytes mxfa_fwd_kvcache_dkdv needs (rules as mxfa_workspace_size). */
+/* Scratch bytes mxfa_fwd_kvcache_dkdv needs: the size query of the two-phase
+ * call (SmallQ FlashAttention README, "aclnn API call"), rules as
+ * mxfa_workspace_size. */
 MXFA_API mxfa_status mxfa_workspace_size_dkdv(int B, int Hq, int Hkv, int Dk,
                                               int Dv, int qLen, int kv_cap,
                                               int causal, int dtype,
                                               int num_splits, size_t *bytes);
 
 /* The plan (path, partitioning, grid, scratch size) for a problem on a
- * device with num_cus compute units (num_cus <= 0 means 256, an MI355X).
- * Pure host code: makes no HIP runtime call, so it works without a GPU. */
+ * device with num_cus compute units (num_cus <= 0 means 256, an MI355X):
+ * the record mxfa_last_plan reports for a call with the same arguments
+ * (num_splits as for mxfa_fwd_kvcache_ws, since a forced partition count
+ * changes the plan; causal and dtype are checked like the execute call's).
+ * It lets a caller see before launching which kernel a problem takes, the
+ * purpose get_last_dispatch_info serves after the fact on the MXFlashAttn
+ * package page (Python API section).  Pure host code: makes no HIP runtime
+ * call, so it works without a GPU. */
 MXFA_API mxfa_status mxfa_plan(int B, int Hq, int Hkv, int D, int qLen,
                                int kv_cap, int causal, int dtype,
                                int num_splits, int num_cus, mxfa_plan_t *plan);
 
-/* The plan of the last successful attention call made by this host thread.
+/* The plan of the last successful attention call made by this host thread:
+ * the analogue of get_last_dispatch_info on the MXFlashAttn package page
+ * (Python API section), whose C500 usage section asks to check which kernel
+ * ran before trusting a throughput figure.
  * Returns MXFA_ERR_INVALID_ARG if plan is NULL or no call has succeeded on
  * this thread yet. */
 MXFA_API mxfa_status mxfa_last_plan(mxfa_plan_t *plan);
 
-/* Timing hook for benchmarks.  After this call, every attention call made by
+/* Timing hook for benchmarks (no passage of the pages defines it).  After this call, every attention call made by
  * this host thread records the HIP event `before` on its stream immediately
  * before the split-KV kernel is enqueued and `after` immediately after it, so
  * hipEventElapsedTime(before, after) is that kernel's duration alone (the
@@ -334,7 +364,10 @@ MXFA_API mxfa_status mxfa_read_probe(const void *src, size_t bytes,
                                      int nontemporal, uint32_t *sink,
                                      int num_cus, void *stream);
 
-/* Static, human-readable text for a status value (never NULL). */
+/* Static, human-readable text for a status value (never NULL).  It takes an
+ * int so that any value, also one outside mxfa_status, can be passed across
+ * the C ABI; unknown values get a generic text.  Explicit errors instead of a
+ * silent fallback follow the limits section of the MXFlashAttn package page. */
 MXFA_API const char *mxfa_status_string(int status);
 
 /* Library version as major * 10000 + minor * 100 + patch. */

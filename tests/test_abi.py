@@ -103,6 +103,7 @@ def _call_ws(num_splits=0, ws=None, ws_bytes=0, **kw):
 INV, UNS = mxfa.MXFA_ERR_INVALID_ARG, mxfa.MXFA_ERR_UNSUPPORTED
 
 
+@pytest.mark.fakeptr
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), INV), (dict(k=0), INV), (dict(v=0), INV), (dict(out=0), INV),
     (dict(q=0x10008), INV), (dict(k=0x20004), INV), (dict(v=0x30002), INV),
@@ -135,6 +136,7 @@ def _call_paged(ws_entry=False, num_splits=0, **kw):
     return m.lib().mxfa_fwd_kvcache_paged(*args, None)
 
 
+@pytest.mark.fakeptr
 @pytest.mark.parametrize("kw,status", [
     (dict(bt=0), INV), (dict(bt=0x60002), INV), (dict(k=0), INV), (dict(q=0), INV),
     (dict(page=0), INV), (dict(page=-16), INV), (dict(max_pages=-1), INV),
@@ -150,6 +152,7 @@ def test_paged_arguments_rejected_before_any_hip_call(kw, status):
     assert _call_paged(ws_entry=True, **kw) == status
 
 
+@pytest.mark.fakeptr
 def test_paged_empty_and_pageless_problems():
     assert _call_paged(B=0) == mxfa.MXFA_OK
     assert _call_paged(qLen=0) == mxfa.MXFA_OK
@@ -181,6 +184,7 @@ def _call_append(paged=False, **kw):
         a["new_len"], a["cap"], a["causal"], a["dtype"], a["num_splits"], None, 0, None)
 
 
+@pytest.mark.fakeptr
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("kw,status", [
     (dict(new_len=-1), INV), (dict(sl=0), INV), (dict(sl=0x90002), INV),
@@ -193,6 +197,7 @@ def test_append_arguments_rejected_before_any_hip_call(paged, kw, status):
     assert _call_append(paged=paged, **kw) == status
 
 
+@pytest.mark.fakeptr
 def test_append_empty_problems():
     assert _call_append(B=0) == mxfa.MXFA_OK
     assert _call_append(paged=True, B=0) == mxfa.MXFA_OK
@@ -214,6 +219,7 @@ def _call_varlen(**kw):
                                    None)
 
 
+@pytest.mark.fakeptr
 @pytest.mark.parametrize("kw,status", [
     (dict(cq=0), INV), (dict(ck=0), INV), (dict(cq=0x90002), INV), (dict(q=0), INV),
     (dict(k=0), INV), (dict(out=0x40004), INV), (dict(total_q=-1), INV),
@@ -225,6 +231,7 @@ def test_varlen_arguments_rejected_before_any_hip_call(kw, status):
     assert _call_varlen(**kw) == status
 
 
+@pytest.mark.fakeptr
 def test_varlen_empty_problems():
     assert _call_varlen(B=0) == mxfa.MXFA_OK
     assert _call_varlen(total_q=0, q=0, out=0) == mxfa.MXFA_OK
@@ -242,6 +249,7 @@ def _call_dkdv(**kw):
                                          a["dtype"], a["num_splits"], None, 0, None)
 
 
+@pytest.mark.fakeptr
 @pytest.mark.parametrize("kw,status", [
     (dict(Dk=0), INV), (dict(Dv=-8), INV), (dict(Dk=100), UNS), (dict(Dv=264), UNS),
     (dict(Dk=4), UNS), (dict(q=0), INV), (dict(v=0x30008), INV), (dict(num_splits=-1), INV),
@@ -269,6 +277,7 @@ def test_plan_routes_head_dims():
                                             ctypes.byref(n)) == INV
 
 
+@pytest.mark.fakeptr
 def test_empty_problem_is_a_no_op():
     assert _call(B=0) == mxfa.MXFA_OK
     assert _call(qLen=0) == mxfa.MXFA_OK
@@ -276,6 +285,7 @@ def test_empty_problem_is_a_no_op():
     assert _call_ws(qLen=0) == mxfa.MXFA_OK
 
 
+@pytest.mark.fakeptr
 def test_ws_rejects_negative_splits_and_misaligned_workspace():
     assert _call_ws(num_splits=-1) == INV
     assert _call_ws(ws=0x70010, ws_bytes=1 << 20) == INV
@@ -412,6 +422,7 @@ def test_plan_rejects_bad_arguments():
     assert m.lib().mxfa_plan(1, 8, 2, 128, 1, 64, 0, 0, 0, 0, None) == INV
 
 
+@pytest.mark.fakeptr
 @pytest.mark.parametrize("src,nbytes,nt,sink,cus", [
     (0, 1 << 20, 1, 0x50000, 0),              # null source
     (0x10000, 1 << 20, 1, 0, 0),              # null sink
@@ -427,3 +438,24 @@ def test_read_probe_rejects_bad_arguments(src, nbytes, nt, sink, cus):
     vp = lambda x: ctypes.c_void_p(x) if x else None
     st = m.lib().mxfa_read_probe(vp(src), nbytes, nt, vp(sink), cus, None)
     assert st == mxfa.MXFA_ERR_INVALID_ARG
+
+
+def test_fake_pointer_tests_with_the_gpu_hidden():
+    """Where a GPU is visible the fake-pointer tests are skipped in this
+    process; here they run in a child process with every GPU hidden, and the
+    child's own collection check skips them again if it still sees one."""
+    import subprocess
+    import sys
+
+    import conftest
+    if not conftest.gpu_visible():
+        pytest.skip("no GPU is visible: the fake-pointer tests run directly")
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1",
+               ROCR_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-m", "pytest", __file__, "-q", "-m", "fakeptr",
+                        "-p", "no:cacheprovider"], env=env, capture_output=True, text=True,
+                       timeout=600)
+    print(r.stdout[-2000:], r.stderr[-2000:])
+    if "skipped" in r.stdout and "passed" not in r.stdout:
+        pytest.skip("the child process still saw a GPU")
+    assert r.returncode == 0, r.stdout[-2000:]
