@@ -37,12 +37,15 @@
  * Arithmetic: 16-bit inputs, fp32 accumulation (as the SmallQ README's
  * algorithm notes prescribe), output rounded to nearest-even.
  *
- * Supported: head dims D that are multiples of 8 up to 256 (the SmallQ
- * README's support range allows any head dim and was verified at 64, 128,
- * 256 and the 192 / 128 split of MLA heads; 64 and 128 are the fast paths,
- * other dims are padded to 192 or 256 inside the matrix-core kernel); any
- * Hq that is a multiple of Hkv; fp16 and bf16.  Other shapes return
- * MXFA_ERR_UNSUPPORTED; nothing falls back silently.
+ * Supported: any head dim D from 1 to 256 (the SmallQ README's support
+ * range allows any head dim of at least 1 and was verified at 64, 128, 256
+ * and the 192 / 128 split of MLA heads; its algorithm notes pad the head dim
+ * on chip).  64 and 128 are the fast paths; other dims are padded to a tile
+ * of 64, 128, 192 or 256 channels inside the matrix-core kernel, and dims
+ * that are not multiples of 8 (rows only 2-byte aligned) are read and
+ * written element by element.  Any Hq that is a multiple of Hkv; fp16 and
+ * bf16.  Other shapes return MXFA_ERR_UNSUPPORTED; nothing falls back
+ * silently.
  *
  * Ownership and threading: the caller owns every buffer.  The library keeps
  * no pointer after a call returns.  Its only mutable state is the
@@ -294,8 +297,8 @@ MXFA_API mxfa_status mxfa_fwd_varlen(const void *q, const void *k,
 /* Different head dims for keys and values (the DeepSeek V3 MLA heads the
  * SmallQ README verifies: K side 192, V side 128): q [B, qLen, Hq, Dk],
  * k_cache [B, kv_cap, Hkv, Dk], v_cache [B, kv_cap, Hkv, Dv], out
- * [B, qLen, Hq, Dv]; the scale is 1/sqrt(Dk).  Dk and Dv are multiples of 8
- * up to 256.  workspace == NULL: scratch from the stream-ordered allocator;
+ * [B, qLen, Hq, Dv]; the scale is 1/sqrt(Dk).  Dk and Dv are any dims from
+ * 1 to 256.  workspace == NULL: scratch from the stream-ordered allocator;
  * otherwise at least mxfa_workspace_size_dkdv bytes.  Otherwise as
  * mxfa_fwd_kvcache_ws. */
 MXFA_API mxfa_status mxfa_fwd_kvcache_dkdv(const void *q, const void *k_cache,

@@ -62,8 +62,8 @@ mxfa_status check_problem(const Problem &p) {
     if (!mul_ok((uint64_t)p.B, (uint64_t)p.qLen, &x) || !mul_ok(x, (uint64_t)p.Hq, &x) ||
         !mul_ok(x, (uint64_t)p.dmax(), &x) || !mul_ok(x, 8, &x) || x > (UINT64_C(1) << 62))
         return MXFA_ERR_INVALID_ARG;
-    // head dims: multiples of 8 (16-byte rows) up to 256
-    if (p.dk() % 8 || p.dv() % 8 || p.dk() > 256 || p.dv() > 256) return MXFA_ERR_UNSUPPORTED;
+    // head dims: any from 1 to 256 (the matrix-core tiles pad them on chip)
+    if (p.dk() > 256 || p.dv() > 256) return MXFA_ERR_UNSUPPORTED;
     if (p.B > kMaxGridYZ) return MXFA_ERR_UNSUPPORTED;
     if (p.page_size > 0) {
         // paged: the pool's byte size must be representable; one page is
@@ -203,12 +203,15 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
         (uint64_t)p.B * (uint64_t)p.kv_cap * p.Hkv * (uint64_t)(p.dk() + p.dv()) * 2;
     const bool valu_stream = p.page_size == 0 && p.dk() == 128 && R == kMfmaMinRows128 &&
                              cache_bytes >= kValuStreamBytes;
+    // head dims that are not multiples of 8: 2-byte aligned rows, element
+    // loads on the matrix-core kernel's 16-row tiles, one kv head per workgroup
+    const bool odd = odd_head_dims(p.dk(), p.dv());
     if ((R >= mfma_min && !valu_stream) || !valu_dims) {
         // many rows per kv head (Q K^T and P V are dense 16-row tiles), or a
         // head shape only the matrix-core kernel's padded tiles hold
         pl.path = MXFA_PATH_MFMA;
         pl.row_block = mfma_row_block(p.dk(), p.dv());
-        if (MXFA_MFMA_SMALL && R <= kMfmaSmallRows && p.dk() <= 128 && p.dv() <= 128)
+        if (odd || (MXFA_MFMA_SMALL && R <= kMfmaSmallRows && p.dk() <= 128 && p.dv() <= 128))
             pl.row_block = kMfmaSmallRows;
         pl.layout = kTokens;
         // two kv heads per workgroup (two waves each) when Hkv is even and
@@ -218,7 +221,7 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
         // from the caches, and pairing heads doubles what those re-reads
         // cycle through: a packed chunked-prefill batch fell from 536 to 313
         // TFLOP/s with pairs, so such problems keep one head per workgroup.
-        if (p.Hkv % kMfmaHeads == 0 && R <= pl.row_block) hpb = kMfmaHeads;
+        if (!odd && p.Hkv % kMfmaHeads == 0 && R <= pl.row_block) hpb = kMfmaHeads;
     } else {
         pl.path = MXFA_PATH_VALU;
         pl.row_block = next_pow2_le8((int)R);
@@ -265,7 +268,7 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     if (num_splits == 0 && S > 1 && p.B <= kMaxBalancedBatch) {
         pl.schedule = kBalanced;
         const int P = num_cus * (pl.path == MXFA_PATH_VALU ? kValuPerCU
-                                 : pl.row_block == kMfmaSmallRows ? 2 : kMfmaPerCU);
+                                 : pl.row_block == kMfmaSmallRows && !odd ? 2 : kMfmaPerCU);
         pl.num_splits = P;
         pl.chunk = 0;
         pl.grid_x = P;
@@ -692,8 +695,8 @@ MXFA_API const char *mxfa_status_string(int status) {
     case MXFA_OK: return "MXFA_OK: success";
     case MXFA_ERR_INVALID_ARG: return "MXFA_ERR_INVALID_ARG: invalid argument";
     case MXFA_ERR_UNSUPPORTED:
-        return "MXFA_ERR_UNSUPPORTED: unsupported shape (head dims must be multiples of 8 up to "
-               "256; see mxfa.h for the other limits)";
+        return "MXFA_ERR_UNSUPPORTED: unsupported shape (head dims up to 256; see mxfa.h for "
+               "the other limits)";
     case MXFA_ERR_WORKSPACE: return "MXFA_ERR_WORKSPACE: workspace missing or too small";
     case MXFA_ERR_HIP: return "MXFA_ERR_HIP: HIP runtime error";
     default: return "unknown mxfa status";

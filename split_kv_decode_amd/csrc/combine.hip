@@ -167,8 +167,15 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(KernelArgs a) {
     const float inv = empty ? 0.f : 1.f / L;
     if (lane < LPG && d0 < a.Dv) {
         uint16_t *outp = (uint16_t *)a.out + (q_token(a, b, i) * a.Hq + h) * a.Dv + d0;
-        *(u32x2 *)outp = u32x2{pack2<DT>(acc[0] * inv, acc[1] * inv),
-                               pack2<DT>(acc[2] * inv, acc[3] * inv)};
+        if (a.Dv % 4 == 0) {
+            *(u32x2 *)outp = u32x2{pack2<DT>(acc[0] * inv, acc[1] * inv),
+                                   pack2<DT>(acc[2] * inv, acc[3] * inv)};
+        } else {
+            // rows only 2-byte aligned: element stores, none past the head
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (d0 + j < a.Dv) outp[j] = (uint16_t)to16<DT>(acc[j] * inv);
+        }
     }
     if (lane == 0 && a.lse) a.lse[lse_index(a, b, h, i)] = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
 }

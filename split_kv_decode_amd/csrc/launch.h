@@ -58,7 +58,7 @@ struct KernelArgs {
     int G;                    // Hq / Hkv
     int R;                    // G * qLen rows per kv head
     int D;                    // VALU kernel: head dim (= Dk = Dv)
-    int Dk, Dv;               // head dims of q / k and of v / out (multiples of 8)
+    int Dk, Dv;               // head dims of q / k and of v / out (1 .. 256)
     int dv_tile;              // channels per row of ws_o (Dv rounded up to the kernel tile)
     int causal;
     int head_block, head_blocks;
@@ -128,8 +128,8 @@ __device__ __forceinline__ size_t lse_index(const KernelArgs &a, int b, int h, i
 hipError_t launch_split_valu(const KernelArgs &a, int dtype, int layout, dim3 grid,
                              hipStream_t stream);
 
-// Matrix-core split kernel tile widths: the head dims (Dk, Dv), multiples of
-// 8 up to 256, are padded to (64, 64), (128, 128), (192, 128) or (256, 256).
+// Matrix-core split kernel tile widths: the head dims (Dk, Dv), 1 to 256,
+// are padded to (64, 64), (128, 128), (192, 128) or (256, 256).
 // 16-row tiles per wave: four up to 128 x 128, two at 192 x 128, one at
 // 256 x 256 (the accumulators, Q and the K / V staging must fit one wave's
 // registers); two LDS stages per wave up to 128 x 128, else one.
@@ -160,6 +160,11 @@ inline __host__ __device__ int mfma_row_block(int dk, int dv) {
 hipError_t launch_split_mfma(const KernelArgs &a, int dtype, dim3 grid, hipStream_t stream);
 hipError_t launch_split_mfma_wide(const KernelArgs &a, int dtype, dim3 grid,
                                   hipStream_t stream);
+// Head dims that are not multiples of 8 (rows only 2-byte aligned): the
+// matrix-core kernel's 16-row tiles with element loads and stores, one kv
+// head per workgroup (row_block = kMfmaSmallRows, head_block = 1).
+inline __host__ __device__ bool odd_head_dims(int dk, int dv) { return (dk % 8) || (dv % 8); }
+hipError_t launch_split_mfma_odd(const KernelArgs &a, int dtype, dim3 grid, hipStream_t stream);
 
 hipError_t launch_combine(const KernelArgs &a, int dtype, hipStream_t stream);
 

@@ -66,6 +66,16 @@
 // written), and only the first Dv output channels are stored.  Wide tiles
 // keep fewer row tiles per wave (32 rows at 192 x 128, 16 at 256 x 256) and
 // one LDS stage, so registers and LDS stay within one workgroup per CU.
+// Any other head dim (ODD: Dk or Dv not a multiple of 8, so head rows are
+// only 2-byte aligned) pads to the same tiles on chip, as the SmallQ
+// README's algorithm notes pad the head dim to 16: every 16-byte chunk is
+// assembled from 16-bit loads, its elements past the head are set to zero
+// (a neighbouring head's or token's values, or the NaN of an unused cache
+// slot, must not reach a product), and outputs are stored element by
+// element so that nothing past the head is written.  These launches use one
+// 16-row tile per wave with K staged in LDS (the loads' 16-bit pieces need
+// twice the registers of a 16-byte load while in flight) and one workgroup
+// per CU.
 #pragma once
 
 #include "device_common.h"
@@ -119,8 +129,28 @@ __device__ __forceinline__ float group_sum(float x) {
     return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
+// The 8 16-bit elements of a head-row chunk whose first element is element
+// e0 of the head, at byte offset `off` (2-byte aligned) of descriptor r, as
+// a 16-byte operand; elements at or past `lim` (the head width) are zero.
+// Every load stays inside the descriptor's range or reads 0 (the range
+// ends at the segment's last token), so the loads are unconditional and
+// the mask is a select, never a product.
+template <int POL>
+__device__ __forceinline__ u32x4 load_chunk_elems(__amdgpu_buffer_rsrc_t r, uint32_t off, int e0,
+                                                  int lim) {
+    uint32_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        h[j] = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2u * j, 0, POL);
+    u32x4 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        x[j] = (e0 + 2 * j < lim ? h[2 * j] : 0u) | ((e0 + 2 * j + 1 < lim ? h[2 * j + 1] : 0u) << 16);
+    return x;
+}
+
 // DK / DV: the tile widths (padded head dims) of K and V; the real widths
-// a.Dk <= DK and a.Dv <= DV are multiples of 8.
+// a.Dk <= DK and a.Dv <= DV are multiples of 8, or any dims with ODD.
 // POL: cache policy of the K/V loads (the streaming one when each K/V byte
 // is read once; 0 when several row blocks of a head read it again).
 // SMALL: one row tile (16 rows) per wave and one LDS stage, for at most 16
@@ -129,8 +159,9 @@ __device__ __forceinline__ float group_sum(float x) {
 // keys x 64 bytes per load instruction) instead of through LDS (the 64-row
 // launches; it matters most when several row blocks of a head re-read its
 // K/V from the caches, where the LDS round trip limits the kernel).
+// ODD: head dims that are not multiples of 8 (with SMALL, without KD).
 template <int DT, int DK, int DV, int HPW, bool PAGED, int POL = MXFA_KV_LOAD_POLICY,
-          bool SMALL = false, bool KD = false>
+          bool SMALL = false, bool KD = false, bool ODD = false>
 struct Mfma {
     using T = MfmaType<DT>;
     typedef typename T::vec vec;
@@ -158,6 +189,7 @@ struct Mfma {
     static constexpr int SWV = (NCHV & (NCHV - 1)) == 0 ? NCHV : 8;
     static_assert(DK % 32 == 0 && DV % 32 == 0 && DK <= 256 && DV <= 256, "tile widths");
     static_assert(NCHK % 8 == 0 && NCHV % 8 == 0, "loads of 4+ chunks stay in one key row group");
+    static_assert(!ODD || (SMALL && !KD), "odd head dims: 16-row tiles, K through LDS");
 
     // LDS: during the tile loop, STG K and V tile pairs per wave; during the
     // merge, each wave's RB x DV block of O as fp32 rows of ORS bytes (16
@@ -262,6 +294,14 @@ struct Mfma {
         }
 
         u32x4 ks[LDK], vs[LDV];
+        // the chunk (of the head row) a lane's load u of K / V covers without
+        // KD: (64 u + lane) % NCH (NCH = 24 at the 192-wide K tile does not
+        // divide 64, so it depends on u)
+        int kch[LDK], vch[LDV];
+#pragma unroll
+        for (int u = 0; u < LDK; ++u) kch[u] = (64 * u + lane) % NCHK;
+#pragma unroll
+        for (int u = 0; u < LDV; ++u) vch[u] = (64 * u + lane) % NCHV;
         // tile index of the wave's i-th tile; indices past the segment are
         // clamped to ntiles, whose keys all lie past t_end (loads read nothing)
         auto tile_of = [&](int i) { return min(sub + WPH * i, ntiles); };
@@ -288,14 +328,16 @@ struct Mfma {
         // the load whose first key is tok, from page entry e, through a
         // descriptor whose range ends at the last token below t_end
         auto page_load = [&](const void *pool, uint32_t tokb, size_t row_elems, int tok,
-                             uint32_t e, uint32_t lane_off) {
+                             uint32_t e, uint32_t lane_off, int e0, int lim) {
             const int pi = tok >> a.log_page;
             const int valid = t_end - (pi << a.log_page);
             const int pg = clampi(__builtin_amdgcn_readfirstlane((int)e), 0, a.num_pages - 1);
             const uint32_t rng = valid <= 0 ? 0u : (uint32_t)min(valid, page) * tokb;
             const __amdgpu_buffer_rsrc_t r = make_rsrc(
                 (const uint16_t *)pool + ((size_t)pg << a.log_page) * row_elems, rng);
-            return load16<POL>(r, (uint32_t)(tok & (page - 1)) * tokb + lane_off);
+            const uint32_t off = (uint32_t)(tok & (page - 1)) * tokb + lane_off;
+            if constexpr (ODD) return load_chunk_elems<POL>(r, off, e0, lim);
+            else return load16<POL>(r, off);
         };
         auto gload_v = [&](int j) {
             const int t0 = PAGED ? t_base + j * kKT : t_lo + j * kKT;
@@ -304,7 +346,9 @@ struct Mfma {
                 const int tok = t0 + 64 * u / NCHV;
                 if constexpr (PAGED)
                     vs[u] = page_load(a.v, vtok, (size_t)a.Hkv * a.Dv, tok, pg_cur[tok - t0 >= 16],
-                                      voff[u]);
+                                      voff[u], 8 * vch[u], a.Dv);
+                else if constexpr (ODD)
+                    vs[u] = load_chunk_elems<POL>(vrsrc, (uint32_t)tok * vtok + voff[u], 8 * vch[u], a.Dv);
                 else
                     vs[u] = load16<POL>(vrsrc, (uint32_t)tok * vtok + voff[u]);
             }
@@ -316,7 +360,9 @@ struct Mfma {
                 const int tok = KD ? t0 + 16 * (u / KK) : t0 + 64 * u / NCHK;
                 if constexpr (PAGED)
                     ks[u] = page_load(a.k, ktok, (size_t)a.Hkv * a.Dk, tok, pg_cur[tok - t0 >= 16],
-                                      koff[u]);
+                                      koff[u], 8 * kch[u], a.Dk);
+                else if constexpr (ODD)
+                    ks[u] = load_chunk_elems<POL>(krsrc, (uint32_t)tok * ktok + koff[u], 8 * kch[u], a.Dk);
                 else
                     ks[u] = load16<POL>(krsrc, (uint32_t)tok * ktok + koff[u]);
             }
@@ -345,9 +391,19 @@ struct Mfma {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 u32x4 x = {0, 0, 0, 0};
-                if (ok && 32 * kk + 8 * g < a.Dk)      // channels past the head: zero
-                    x = *(const u32x4 *)((const uint16_t *)a.q +
-                                         ((qtok0 + qi) * a.Hq + qh) * a.Dk + 32 * kk + 8 * g);
+                const uint16_t *qrow = (const uint16_t *)a.q + ((qtok0 + qi) * a.Hq + qh) * a.Dk;
+                if constexpr (ODD) {
+                    // 2-byte aligned rows: element loads, channels past the head zero
+                    const int e0 = 32 * kk + 8 * g;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t lo = ok && e0 + 2 * j < a.Dk ? qrow[e0 + 2 * j] : 0u;
+                        const uint32_t hi = ok && e0 + 2 * j + 1 < a.Dk ? qrow[e0 + 2 * j + 1] : 0u;
+                        x[j] = lo | (hi << 16);
+                    }
+                } else if (ok && 32 * kk + 8 * g < a.Dk) {   // channels past the head: zero
+                    x = *(const u32x4 *)(qrow + 32 * kk + 8 * g);
+                }
                 qf[rt][kk] = __builtin_bit_cast(vec, x);
             }
         }
@@ -556,8 +612,14 @@ struct Mfma {
                     const int qi = row / a.G;
                     const int qh = kvh * a.G + row % a.G;
                     uint16_t *op = (uint16_t *)a.out + ((qtok0 + qi) * a.Hq + qh) * a.Dv;
-                    if (c0 < a.Dv)                     // channels past the head: not written
+                    if constexpr (ODD) {
+                        // 2-byte aligned rows: element stores, none past the head
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (c0 + e < a.Dv) op[c0 + e] = (uint16_t)to16<DT>(acc[e]);
+                    } else if (c0 < a.Dv) {            // channels past the head: not written
                         *(u32x2 *)(op + c0) = u32x2{pack2<DT>(acc[0], acc[1]), pack2<DT>(acc[2], acc[3])};
+                    }
                 } else {
                     const size_t e = ((size_t)slot * HPW + hx) * RB + rloc;
                     *(f32x4 *)(a.ws_o + e * DV + c0) = acc;
@@ -571,11 +633,12 @@ struct Mfma {
 // One workgroup per CU, one wave per SIMD: each wave keeps its head's rows
 // of accumulators and one K/V tile in registers.
 
-template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED, int POL, bool SMALL, bool KD>
+template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED, int POL, bool SMALL, bool KD,
+          bool ODD = false>
 __global__ __launch_bounds__(kMWaves * 64)
-__attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1, SMALL ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu(SMALL && !ODD ? 2 : 1, SMALL && !ODD ? 2 : 1)))
 void split_kv_mfma_kernel(KernelArgs a) {
-    using M = Mfma<DT, DK, DV, HPW, PAGED, POL, SMALL, KD>;
+    using M = Mfma<DT, DK, DV, HPW, PAGED, POL, SMALL, KD, ODD>;
     __shared__ __attribute__((aligned(16))) typename M::Smem sm;
     drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
                                  bool whole) {
@@ -583,14 +646,33 @@ void split_kv_mfma_kernel(KernelArgs a) {
     });
 }
 
-template <int DT, int DK, int DV, int HPW, int POL, bool SMALL = false, bool KD = false>
+template <int DT, int DK, int DV, int HPW, int POL, bool SMALL = false, bool KD = false,
+          bool ODD = false>
 const void *kernel_for(const KernelArgs &a) {
     const bool paged = a.block_table != nullptr;
     return a.schedule == kBalanced
-               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true, POL, SMALL, KD>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false, POL, SMALL, KD>)
-               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true, POL, SMALL, KD>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false, POL, SMALL, KD>);
+               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true, POL, SMALL, KD, ODD>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false, POL, SMALL, KD, ODD>)
+               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true, POL, SMALL, KD, ODD>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false, POL, SMALL, KD, ODD>);
+}
+
+// Head dims that are not multiples of 8: 16-row tiles, one kv head per
+// workgroup, K through LDS, element loads and stores.
+template <int DT, int DK, int DV>
+hipError_t launch_odd_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
+    if (a.row_block != kMfmaSmallRows || a.Dk > DK || a.Dv > DV || a.head_block != 1)
+        return hipErrorInvalidValue;
+    KernelArgs args = a;
+    void *kargs[] = {&args};
+    const void *fn = kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY, true, false, true>(a);
+    return hipLaunchKernel(fn, grid, dim3(kMWaves * 64), kargs, 0, stream);
+}
+
+template <int DK, int DV>
+hipError_t launch_odd_dims(const KernelArgs &a, int dtype, dim3 grid, hipStream_t stream) {
+    return dtype == kFp16 ? launch_odd_t<kFp16, DK, DV>(a, grid, stream)
+                          : launch_odd_t<kBf16, DK, DV>(a, grid, stream);
 }
 
 template <int DT, int DK, int DV>

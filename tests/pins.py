@@ -83,6 +83,10 @@ _TINY = [
     (2, 4, 2, 2, 64, 9, [0, 9], False, "bf16"),
     (1, 5, 8, 2, 16, 12, [3], True, "fp16"),    # causal with n < qLen: empty rows
     (2, 2, 8, 8, 8, 6, [6, 5], True, "bf16"),
+    # head dims that are not multiples of 8 (the support range allows any)
+    (2, 3, 4, 2, 1, 8, [8, 2], True, "fp16"),
+    (1, 2, 6, 3, 5, 11, None, False, "bf16"),
+    (2, 4, 4, 1, 17, 10, [10, 4], True, "bf16"),
 ]
 
 
@@ -110,7 +114,9 @@ def pin_torch_sdpa_fp64(lib_path):
             (1, 4, 8, 2, 64, 40, 40, True, "bf16"),
             (2, 8, 8, 1, 128, 70, 70, True, "fp16"),
             (1, 3, 4, 4, 32, 50, 50, False, "fp16"),
-            (1, 2, 6, 3, 16, 30, 30, True, "bf16")]:
+            (1, 2, 6, 3, 16, 30, 30, True, "bf16"),
+            (1, 3, 4, 2, 3, 20, 20, True, "fp16"),
+            (1, 2, 4, 1, 129, 25, 25, False, "bf16")]:
         q = _rand((B, qLen, Hq, D), dt, g)
         k = _rand((B, cap, Hkv, D), dt, g)
         v = _rand((B, cap, Hkv, D), dt, g)
@@ -143,7 +149,9 @@ def pin_separate_key_and_value_dims(lib_path):
     for (B, qLen, Hq, Hkv, Dk, Dv, cap, lens, causal, dt) in [
             (2, 3, 4, 2, 24, 16, 9, [9, 4], True, "bf16"),
             (1, 2, 2, 1, 16, 40, 7, None, False, "fp16"),
-            (1, 4, 8, 2, 192, 128, 30, [30], True, "bf16")]:
+            (1, 4, 8, 2, 192, 128, 30, [30], True, "bf16"),
+            (2, 2, 4, 2, 3, 13, 8, [8, 3], True, "fp16"),
+            (1, 3, 2, 1, 17, 9, 6, None, False, "bf16")]:
         q = _rand((B, qLen, Hq, Dk), dt, g)
         k = _rand((B, cap, Hkv, Dk), dt, g)
         v = _rand((B, cap, Hkv, Dv), dt, g)

@@ -112,7 +112,7 @@ INV, UNS = mxfa.MXFA_ERR_INVALID_ARG, mxfa.MXFA_ERR_UNSUPPORTED
     (dict(Hkv=0), INV), (dict(D=0), INV), (dict(Hq=6, Hkv=4), INV),
     (dict(causal=2), INV), (dict(causal=-1), INV), (dict(dtype=2), INV), (dict(dtype=-1), INV),
     (dict(B=2**30, cap=2**30), INV),                       # byte size overflow
-    (dict(D=100), UNS), (dict(D=264), UNS), (dict(D=4), UNS), (dict(B=70000), UNS),
+    (dict(D=257), UNS), (dict(D=264), UNS), (dict(D=300), UNS), (dict(B=70000), UNS),
     (dict(cap=2**16, Hq=128, Hkv=128), UNS),               # cache past 2^30 bytes per sequence
     (dict(cap=1, Hq=8192, Hkv=8192), UNS),                 # 1024-token slack past 2^30 bytes
 ])
@@ -145,7 +145,7 @@ def _call_paged(ws_entry=False, num_splits=0, **kw):
     (dict(page=1 << 17, Hq=64, Hkv=64), UNS),              # one page past 2^30 bytes
     (dict(page=1 << 20, max_pages=1 << 12), UNS),          # logical capacity past INT_MAX
     (dict(num_pages=1 << 40 >> 20, page=1 << 20, Hq=64, Hkv=64, max_pages=1), UNS),
-    (dict(D=100), UNS), (dict(Hq=6, Hkv=4), INV), (dict(causal=3), INV), (dict(dtype=5), INV),
+    (dict(D=260), UNS), (dict(Hq=6, Hkv=4), INV), (dict(causal=3), INV), (dict(dtype=5), INV),
 ])
 def test_paged_arguments_rejected_before_any_hip_call(kw, status):
     assert _call_paged(**kw) == status
@@ -189,7 +189,7 @@ def _call_append(paged=False, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(new_len=-1), INV), (dict(sl=0), INV), (dict(sl=0x90002), INV),
     (dict(kn=0), INV), (dict(vn=0), INV), (dict(kn=0x70008), INV),
-    (dict(k=0), INV), (dict(num_splits=-2), INV), (dict(D=84), UNS),
+    (dict(k=0), INV), (dict(num_splits=-2), INV), (dict(D=272), UNS),
     (dict(qLen=0, k=0), INV),                    # the cache is still written
     (dict(new_len=2 ** 30, B=2 ** 15, Hkv=1024, Hq=1024), INV),   # k_new byte size
 ])
@@ -224,7 +224,7 @@ def _call_varlen(**kw):
     (dict(cq=0), INV), (dict(ck=0), INV), (dict(cq=0x90002), INV), (dict(q=0), INV),
     (dict(k=0), INV), (dict(out=0x40004), INV), (dict(total_q=-1), INV),
     (dict(total_k=-1), INV), (dict(max_q=-1), INV), (dict(max_k=-1), INV),
-    (dict(num_splits=-1), INV), (dict(D=36), UNS), (dict(Hq=3), INV),
+    (dict(num_splits=-1), INV), (dict(D=258), UNS), (dict(Hq=3), INV),
     (dict(max_k=1 << 22, Hkv=128, Hq=128), UNS),           # one sequence past 2^30 bytes
 ])
 def test_varlen_arguments_rejected_before_any_hip_call(kw, status):
@@ -251,8 +251,8 @@ def _call_dkdv(**kw):
 
 @pytest.mark.fakeptr
 @pytest.mark.parametrize("kw,status", [
-    (dict(Dk=0), INV), (dict(Dv=-8), INV), (dict(Dk=100), UNS), (dict(Dv=264), UNS),
-    (dict(Dk=4), UNS), (dict(q=0), INV), (dict(v=0x30008), INV), (dict(num_splits=-1), INV),
+    (dict(Dk=0), INV), (dict(Dv=-8), INV), (dict(Dk=257), UNS), (dict(Dv=264), UNS),
+    (dict(Dv=300), UNS), (dict(q=0), INV), (dict(v=0x30008), INV), (dict(num_splits=-1), INV),
     (dict(cap=1 << 20, Hkv=8, Hq=8, Dk=256), UNS),         # a sequence past 2^30 bytes
 ])
 def test_dkdv_arguments_rejected_before_any_hip_call(kw, status):
@@ -272,6 +272,14 @@ def test_plan_routes_head_dims():
     for D, rb in ((96, 64), (256, 16), (200, 16)):
         p = m.plan(4, 64, 2, D, 2, 4096, 0, 1)                   # 64 rows per kv head
         assert p.path == 1 and p.row_block == rb, D
+    # head dims that are not multiples of 8: 16-row tiles, one kv head per
+    # workgroup, one workgroup per CU in the balanced grid
+    for D in (1, 3, 17, 36, 100, 129, 130, 255):
+        for G, qLen in ((1, 1), (4, 1), (8, 8)):
+            p = m.plan(4, 2 * G, 2, D, qLen, 4096, 0, 1, num_cus=256)
+            assert (p.path, p.row_block, p.head_block) == (1, 16, 1), (D, G, qLen)
+            assert p.schedule == 0 or p.grid_x == 256, (D, G, qLen)
+    assert m.plan(1, 8, 2, 256, 1, 64, 0, 1).row_block == 16
     n = ctypes.c_size_t()
     assert m.lib().mxfa_workspace_size_dkdv(2, 8, 2, 192, 128, 1, 64, 0, 0, -1,
                                             ctypes.byref(n)) == INV
@@ -296,7 +304,7 @@ def test_workspace_size_argument_checks():
     L = m.lib()
     assert L.mxfa_workspace_size(1, 8, 2, 128, 1, 64, 0, 0, 0, None) == INV
     assert L.mxfa_workspace_size(1, 8, 3, 128, 1, 64, 0, 0, 0, ctypes.byref(n)) == INV
-    assert L.mxfa_workspace_size(1, 8, 2, 84, 1, 64, 0, 0, 0, ctypes.byref(n)) == UNS
+    assert L.mxfa_workspace_size(1, 8, 2, 300, 1, 64, 0, 0, 0, ctypes.byref(n)) == UNS
     assert L.mxfa_workspace_size(1, 8, 2, 128, 1, 64, 0, 0, -3, ctypes.byref(n)) == INV
 
 
@@ -333,6 +341,14 @@ def test_plan_invariants_over_random_shapes(B, G, Hkv, D, qLen, cap, causal, dt,
     check_plan(B, G * Hkv, Hkv, D, qLen, cap, causal, dt, num_splits, cus)
 
 
+@settings(max_examples=200, deadline=None, derandomize=True)
+@given(B=st.integers(1, 40), G=st.sampled_from([1, 2, 4, 8]), Hkv=st.integers(1, 8),
+       D=st.integers(1, 256), qLen=st.integers(1, 20), cap=st.integers(0, 20000),
+       causal=st.integers(0, 1), num_splits=st.sampled_from([0, 0, 1, 3, 64]))
+def test_plan_invariants_over_any_head_dim(B, G, Hkv, D, qLen, cap, causal, num_splits):
+    check_plan(B, G * Hkv, Hkv, D, qLen, cap, causal, 1, num_splits)
+
+
 def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
     """The plan routes the shape to the right kernel, covers every cache
     position with a non-empty partition and sizes the scratch for every
@@ -342,7 +358,16 @@ def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
     assert p.rows == (Hq // Hkv) * qLen
     cache_bytes = B * cap * Hkv * D * 2 * 2
     valu_stream = D == 128 and p.rows == 4 and cache_bytes >= 256 << 20
-    if p.rows >= (4 if D == 128 else 8) and not valu_stream:
+    if D % 8:
+        # not a multiple of 8: 16-row tiles, one kv head per workgroup
+        assert p.path == 1 and p.row_block == 16 and p.head_block == 1
+    elif D not in (64, 128):
+        # other dims: padded matrix-core tiles (64 rows up to 128, 16 at 256)
+        tile = 64 if D <= 64 else 128 if D <= 128 else 256
+        rb = 16 if (p.rows <= 16 and tile <= 128) or tile == 256 else 64
+        pair = Hkv % 2 == 0 and p.rows <= rb
+        assert p.path == 1 and p.row_block == rb and p.head_block == (2 if pair else 1)
+    elif p.rows >= (4 if D == 128 else 8) and not valu_stream:
         # matrix-core kernel: 16-row blocks up to 16 rows, else 64; two kv
         # heads per workgroup when Hkv is even and one block holds every row
         rb = 16 if p.rows <= 16 else 64
@@ -353,11 +378,13 @@ def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
         assert p.head_block in (1, 4, 8, 16)
     assert Hkv % p.head_block == 0
     streams = B * (Hkv // p.head_block) * -(-p.rows // p.row_block)
-    entry = p.head_block * p.row_block * (D + 1) * 4
+    tile_v = D if p.path == 0 else (64 if D <= 64 else 128 if D <= 128 else 256)
+    entry = p.head_block * p.row_block * (tile_v + 1) * 4
     if p.schedule == 1:                      # balanced: planner's own choice only
         assert num_splits == 0 and p.combine == 1 and p.chunk == 0
         assert (p.grid_x, p.grid_y, p.grid_z) == (p.num_splits, 1, 1)
-        assert p.grid_x == p.num_cus * (2 if p.path == 1 and p.row_block == 16 else 1)
+        assert p.grid_x == p.num_cus * (2 if p.path == 1 and p.row_block == 16 and D % 8 == 0
+                                        else 1)
         assert p.workspace_bytes >= (p.num_splits + streams) * entry + (B + 2) * 8
         return
     S, C = p.num_splits, p.chunk
@@ -416,7 +443,7 @@ def test_plan_fills_the_chip_at_low_batch():
 
 def test_plan_rejects_bad_arguments():
     with pytest.raises(m.MxfaError):
-        m.plan(1, 8, 2, 100, 1, 64)
+        m.plan(1, 8, 2, 300, 1, 64)
     with pytest.raises(m.MxfaError):
         m.plan(1, 8, 2, 128, 1, 64, num_splits=-1)
     assert m.lib().mxfa_plan(1, 8, 2, 128, 1, 64, 0, 0, 0, 0, None) == INV
