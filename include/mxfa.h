@@ -178,6 +178,31 @@ MXFA_API mxfa_status mxfa_workspace_size(int B, int Hq, int Hkv, int D,
                                          int dtype, int num_splits,
                                          size_t *bytes);
 
+/* Largest scratch, in bytes, that mxfa_fwd_kvcache_noalloc can use. */
+#define MXFA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Allocation-free variant of mxfa_fwd_kvcache_ws, for callers that cannot
+ * allocate device memory during the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments and
+ * results as mxfa_fwd_kvcache_ws without the workspace arguments: the
+ * partial results go to a fixed scratch array of MXFA_NOALLOC_SCRATCH_BYTES
+ * in device memory that the library holds on every GPU it runs on until the
+ * process ends.  The call makes no allocation (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks up that
+ * device's array once.  A problem whose plan needs more scratch than the
+ * array holds (mxfa_workspace_size reports the need) returns
+ * MXFA_ERR_WORKSPACE before anything is enqueued.  Nothing in the array has
+ * to start at zero: every value a call reads was written earlier in the same
+ * call.  All calls on one GPU share the array, so calls that may overlap on
+ * one GPU (other streams, other host threads) race on it and must be
+ * ordered by the caller. */
+MXFA_API mxfa_status mxfa_fwd_kvcache_noalloc(const void *q, const void *k_cache,
+                                              const void *v_cache,
+                                              const int32_t *cache_seqlens, void *out,
+                                              float *lse, int B, int Hq, int Hkv, int D,
+                                              int qLen, int kv_cap, int causal, int dtype,
+                                              int num_splits, void *stream);
+
 /* Paged KV cache.  The MXFlashAttn sdist README lists a paged KV cache among
  * its implemented layouts (capability matrix) and describes its kernel as a
  * split-KV paged decode kernel (introduction); the pages give no layout, so

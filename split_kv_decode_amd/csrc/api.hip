@@ -36,6 +36,15 @@ struct Problem {
     int dmax() const { return dk() > dv() ? dk() : dv(); }
 };
 
+// Scratch of the allocation-free entry point (mxfa_fwd_kvcache_noalloc): a
+// fixed array in device memory, one copy per GPU the library is loaded on,
+// held until the process ends.  Host code never uses its name as an address
+// (on the host it is only a stand-in); the device address of each GPU's copy
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and is what kernels and copies are given.
+static __device__ __align__(256) unsigned char scratch[MXFA_NOALLOC_SCRATCH_BYTES];
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
 thread_local mxfa_plan_t t_last_plan;
 thread_local bool t_has_last = false;
 thread_local hipEvent_t t_ev_before = nullptr;
@@ -675,6 +684,34 @@ MXFA_API mxfa_status mxfa_fwd_kvcache_dkdv(const void *q, const void *k_cache,
     return execute(q, k_cache, v_cache, cache_seqlens, nullptr, nullptr, nullptr, out, lse, p,
                    num_splits, workspace, workspace_bytes, workspace == nullptr,
                    (hipStream_t)stream);
+}
+
+MXFA_API mxfa_status mxfa_fwd_kvcache_noalloc(const void *q, const void *k_cache,
+                                              const void *v_cache, const int32_t *cache_seqlens,
+                                              void *out, float *lse, int B, int Hq, int Hkv,
+                                              int D, int qLen, int kv_cap, int causal, int dtype,
+                                              int num_splits, void *stream) {
+    const Problem p{B, Hq, Hkv, D, qLen, kv_cap, causal, dtype};
+    mxfa_status st = check_problem(p);
+    if (st != MXFA_OK) return st;
+    if (num_splits < 0) return MXFA_ERR_INVALID_ARG;
+    if (B == 0 || qLen == 0) return MXFA_OK;
+    st = check_pointers(q, k_cache, v_cache, cache_seqlens, out, lse, kv_cap);
+    if (st != MXFA_OK) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MXFA_ERR_HIP;
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        // first call on this device (it is current): the device address of
+        // its copy of the array; a concurrent first call stores the same value
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return MXFA_ERR_HIP;
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    // execute() plans first and returns MXFA_ERR_WORKSPACE, before any launch,
+    // when the plan needs more scratch than the array holds
+    return execute(q, k_cache, v_cache, cache_seqlens, nullptr, nullptr, nullptr, out, lse, p,
+                   num_splits, ptr, MXFA_NOALLOC_SCRATCH_BYTES, false, (hipStream_t)stream);
 }
 
 MXFA_API mxfa_status mxfa_last_plan(mxfa_plan_t *plan) {

@@ -15,11 +15,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmxfa.so")
 
 MXFA_OK, MXFA_ERR_INVALID_ARG, MXFA_ERR_UNSUPPORTED, MXFA_ERR_WORKSPACE, MXFA_ERR_HIP = range(5)
+NOALLOC_SCRATCH_BYTES = 32 << 20      # MXFA_NOALLOC_SCRATCH_BYTES in include/mxfa.h
 MXFA_FP16, MXFA_BF16 = 0, 1
 PATH_NAMES = {0: "valu", 1: "mfma"}
 
 # every symbol include/mxfa.h declares
 EXPORTS = ("mxfa_fwd_kvcache", "mxfa_fwd_kvcache_ws", "mxfa_workspace_size",
+           "mxfa_fwd_kvcache_noalloc",
            "mxfa_fwd_kvcache_paged", "mxfa_fwd_kvcache_paged_ws", "mxfa_workspace_size_paged",
            "mxfa_fwd_kvcache_append", "mxfa_fwd_kvcache_paged_append", "mxfa_fwd_varlen",
            "mxfa_fwd_kvcache_dkdv", "mxfa_workspace_size_dkdv",
@@ -95,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.mxfa_fwd_kvcache.restype = ci
     L.mxfa_fwd_kvcache_ws.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 9 + [vp, sz, vp]
     L.mxfa_fwd_kvcache_ws.restype = ci
+    L.mxfa_fwd_kvcache_noalloc.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 9 + [vp]
+    L.mxfa_fwd_kvcache_noalloc.restype = ci
     L.mxfa_workspace_size.argtypes = [ci] * 9 + [ctypes.POINTER(sz)]
     L.mxfa_workspace_size.restype = ci
     L.mxfa_fwd_kvcache_paged.argtypes = [vp] * 7 + [ci] * 10 + [vp]
@@ -197,15 +201,16 @@ def _dtype_code(t) -> int:
 
 def fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
                 out=None, lse=None, return_lse: bool = True, num_splits: int = 0,
-                workspace=None, stream=None, prepare: bool = False):
+                workspace=None, stream=None, prepare: bool = False, noalloc: bool = False):
     """Decode attention on the current HIP stream; returns (out, lse), or with
     prepare=True a PreparedCall that enqueues the call on each run().
 
     q [B, qLen, Hq, D]; k_cache, v_cache [B, kv_cap, Hkv, D] (fp16 or bf16,
     contiguous, on one GPU); cache_seqlens int32 [B] or None.  With
     num_splits > 0 or an explicit workspace (a uint8 tensor), the
-    caller-workspace entry point is used; otherwise the library allocates
-    its scratch on the stream.
+    caller-workspace entry point is used; with noalloc=True the
+    allocation-free one (the library's fixed scratch array; no workspace);
+    otherwise the library allocates its scratch on the stream.
     """
     import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
@@ -240,7 +245,12 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     args = (ptr(q), ptr(k_cache), ptr(v_cache), ptr(cache_seqlens), ptr(out), ptr(lse),
             B, Hq, Hkv, D, qLen, kv_cap, int(bool(causal)), dt)
-    if workspace is None and num_splits == 0:
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc=True uses the library's own scratch: pass no workspace")
+        fn = lib().mxfa_fwd_kvcache_noalloc
+        full = (*args, int(num_splits), ctypes.c_void_p(stream))
+    elif workspace is None and num_splits == 0:
         fn, full = lib().mxfa_fwd_kvcache, (*args, ctypes.c_void_p(stream))
     else:
         if workspace is None:
@@ -250,7 +260,8 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, causal: bool = False,
         fn = lib().mxfa_fwd_kvcache_ws
         full = (*args, int(num_splits), ptr(workspace),
                 workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
-    call = PreparedCall(fn, full, "mxfa_fwd_kvcache", q.device.index, out, lse,
+    name = "mxfa_fwd_kvcache_noalloc" if noalloc else "mxfa_fwd_kvcache"
+    call = PreparedCall(fn, full, name, q.device.index, out, lse,
                         (q, k_cache, v_cache, cache_seqlens, workspace))
     return call if prepare else call.run()
 
