@@ -94,11 +94,13 @@ def _kernel_rows(csv_path):
         return list(csv.DictReader(f))
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands):
+def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma_dir=None):
     """Turn rocprofv3 outputs (kernel-trace stats, FETCH_SIZE pass, WRITE_SIZE
-    pass, each of a bench run with --copy-calibration) into a short summary
-    under profiles/ and the per-launch traffic record bench.py reports.
-    The counters are scaled by what they read for the 1 GiB device copy."""
+    pass, each of a bench run with --copy-calibration, and for the matrix-core
+    kernel a MfmaUtil / MfmaFlopsBF16 / MfmaFlopsF16 pass) into a short
+    summary under profiles/ and the per-launch traffic record bench.py
+    reports.  The traffic counters are scaled by what they read for the 1 GiB
+    device copy."""
     import statistics
     stats = _kernel_rows(os.path.join(trace_dir, "run_kernel_stats.csv"))
     fetch = _kernel_rows(os.path.join(fetch_dir, "run_counter_collection.csv"))
@@ -159,6 +161,26 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands):
         lines.append(f"- merge kernel: raw FETCH_SIZE {fmr / 1024:.0f} KiB, WRITE_SIZE "
                      f"{wmr / 1024:.0f} KiB; scaled fetch {fmr * f_scale / 1e6:.2f} MB, write "
                      f"{wmr * w_scale / 1e6:.2f} MB per launch")
+    mfma_rec = None
+    if mfma_dir:
+        rows = _kernel_rows(os.path.join(mfma_dir, "run_counter_collection.csv"))
+        by = {}
+        for r in rows:
+            if "split_kv_" in r["Kernel_Name"]:
+                by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        util = statistics.median(by["MfmaUtil"]) if "MfmaUtil" in by else None
+        fl = sum(statistics.median(by[k]) for k in ("MfmaFlopsBF16", "MfmaFlopsF16") if k in by)
+        pairs = wl.visible_pairs(w, lens)
+        alg_fl = 4 * w.D * pairs
+        lines += ["", "## Matrix cores (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 MfmaFlopsF16)", "",
+                  f"- MfmaUtil (MFMA busy cycles / (GPU active cycles x SIMDs)): {util:.2f}%"
+                  if util is not None else "- MfmaUtil: not reported",
+                  f"- MFMA flops per launch from the counters: {fl / 1e9:.2f} GFLOP; the "
+                  f"attention's algorithmic flops (4 D per visible (row, key) pair): "
+                  f"{alg_fl / 1e9:.2f} GFLOP (the counters also count padded rows and keys)",
+                  f"- algorithmic flops / trace average / 2.5 PFLOP/s: "
+                  f"{100 * alg_fl / (avg_ns * 1e-9) / 2.5e15:.2f}%"]
+        mfma_rec = {"mfma_util_pct": util, "mfma_flops": fl, "algorithmic_flops": alg_fl}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     path = os.path.join(ROOT, "profiles", f"{kname}_{workload}.md")
     with open(path, "w") as f:
@@ -172,6 +194,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands):
                      "bytes_per_launch": int(round(f_split + w_split)),
                      "fetch_bytes": int(round(f_split)), "write_bytes": int(round(w_split)),
                      "fetch_raw_kib": round(f_raw / 1024, 1), "write_raw_kib": round(w_raw / 1024, 1),
+                     "mfma": mfma_rec,
                      "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -310,8 +333,9 @@ def parse():
                          "decode workloads are measured too and summarised under 'configs')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"),
-                    help="summarize rocprofv3 output directories into profiles/ (no GPU)")
+    ap.add_argument("--summarize-profiles", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 output directories TRACE FETCH WRITE [MFMA] "
+                         "into profiles/ (no GPU)")
     ap.add_argument("--profile-command", action="append", default=[],
                     help="command line recorded in the profile summary")
     return ap.parse_args()
@@ -320,7 +344,11 @@ def parse():
 def main():
     args = parse()
     if args.summarize_profiles:
-        summarize_profiles(*args.summarize_profiles, args.workload, args.profile_command)
+        d = args.summarize_profiles
+        if len(d) not in (3, 4):
+            sys.exit("--summarize-profiles takes TRACE FETCH WRITE [MFMA]")
+        summarize_profiles(d[0], d[1], d[2], args.workload, args.profile_command,
+                           d[3] if len(d) == 4 else None)
         return
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
