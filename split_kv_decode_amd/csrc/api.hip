@@ -186,14 +186,14 @@ size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *fp) {
     constexpr int kChunkAlign = 64;
     constexpr int kTargetPerCU = 8;
-    // workgroups per CU in the balanced grid: for the VALU kernel one with
-    // contiguous caches (1-7% faster than two on MHA and GQA-2 decode batches
-    // of 0.5-2 GB, 0.5-0.7 us faster on the SmallQ calls, whose merge then
-    // reads half as many partials) and two with paged ones (a step's page
-    // lookup is waited for in the loop: 257 against 294 us on a 2 GB MHA
-    // batch in 16-token pages); two for the matrix-core kernel's 16-row
+    // workgroups per CU in the balanced grid: for the VALU kernel one (1-7%
+    // faster than two on MHA and GQA-2 decode batches of 0.5-2 GB, 0.5-0.7 us
+    // faster on the SmallQ calls, whose merge then reads half as many
+    // partials; through pages too, since each step's page is requested a step
+    // ahead: paged SmallQ q1/q2 calls 0.6-1.3 us faster, the paged Qwen3-8B
+    // batch 336 against 349 us); two for the matrix-core kernel's 16-row
     // variant, one for its 64-row tiles (their LDS and registers fill the CU)
-    const int kValuPerCU = p.page_size > 0 ? 2 : 1;
+    const int kValuPerCU = 1;
     constexpr int kMfmaPerCU = 1;
     mxfa_plan_t pl;
     std::memset(&pl, 0, sizeof(pl));
@@ -205,12 +205,11 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     int hpb = 1;
     const bool valu_dims = p.dk() == p.dv() && (p.dk() == 64 || p.dk() == 128);
     const int mfma_min = p.dk() == 128 ? kMfmaMinRows128 : kMfmaMinRows;
-    // at exactly the 128-dim threshold, large contiguous caches stream faster
-    // through the VALU kernel (launch.h records the crossover); paged ones
-    // keep the matrix-core kernel, whose page lookups run a tile ahead
+    // at exactly the 128-dim threshold, large caches (contiguous or paged)
+    // stream faster through the VALU kernel (launch.h records the crossover)
     const uint64_t cache_bytes =
         (uint64_t)p.B * (uint64_t)p.kv_cap * p.Hkv * (uint64_t)(p.dk() + p.dv()) * 2;
-    const bool valu_stream = p.page_size == 0 && p.dk() == 128 && R == kMfmaMinRows128 &&
+    const bool valu_stream = p.dk() == 128 && R == kMfmaMinRows128 &&
                              cache_bytes >= kValuStreamBytes;
     // head dims that are not multiples of 8: 2-byte aligned rows, element
     // loads on the matrix-core kernel's 16-row tiles, one kv head per workgroup

@@ -62,8 +62,9 @@
 // Paged caches.  With a block table, token j of sequence b is row j % page of
 // page block_table[b][j / page].  Steps are then aligned to multiples of
 // TSTEP tokens (at most 16, and page >= 16), so the tokens of one step lie in
-// one page: the page is looked up once per step (a scalar load) and the step
-// reads through a buffer descriptor whose range ends at the page's last valid
+// one page: the page is looked up once per step (a vector load of its
+// block-table entry, issued one step of the wave ahead) and the step reads
+// through a buffer descriptor whose range ends at the page's last valid
 // token.  Tokens of the first step that precede the segment are masked.
 #include "device_common.h"
 #include "launch.h"
@@ -229,18 +230,33 @@ struct Valu {
             voff[u] = lane_base + (uint32_t)(u * TSUB + ts) * tok_bytes;
         }
 
+        // paged: the block-table entry of each step is read with a vector load
+        // one load step of the wave ahead (tracked with the K/V loads, so the
+        // wait for it never waits for LDS traffic or for loads issued after
+        // it), through a descriptor that ends at the entry of the last page
+        // holding a token below t_hi: entries past it read 0 and belong to
+        // steps that load nothing
+        const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(
+            PAGED ? (const void *)(a.block_table + (size_t)b * a.max_pages) : nullptr,
+            PAGED ? (uint32_t)((t_hi + (1 << a.log_page) - 1) >> a.log_page) * 4u : 0u);
+        auto fetch_entry = [&](int st) -> uint32_t {
+            return __builtin_amdgcn_raw_buffer_load_b32(
+                bt_rsrc, (uint32_t)((t_base + st * TSTEP) >> a.log_page) * 4u, 0, 0);
+        };
+        uint32_t e_next = PAGED ? fetch_entry(ti) : 0u;    // the wave's first step
+
         auto load_step = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[U]) {
             if constexpr (PAGED) {
-                // the step's page; its descriptors end at the last token
-                // below t_hi (no range when the step lies past it)
+                // the step's page (its entry was requested one step ahead, and
+                // the next step's is requested now); its descriptors end at the
+                // last token below t_hi (no range when the step lies past it)
+                const uint32_t e = e_next;
+                e_next = fetch_entry(st + TI);
                 const int tb = t_base + st * TSTEP;
                 const int pi = tb >> a.log_page;
                 const int valid = t_hi - (pi << a.log_page);
                 const int page = 1 << a.log_page;
-                int pg = 0;
-                if (valid > 0)
-                    pg = clampi(a.block_table[(size_t)b * a.max_pages + pi], 0, a.num_pages - 1);
-                pg = __builtin_amdgcn_readfirstlane(pg);
+                const int pg = clampi(__builtin_amdgcn_readfirstlane((int)e), 0, a.num_pages - 1);
                 const uint32_t rng = valid <= 0 ? 0u : (uint32_t)min(valid, page) * tok_bytes;
                 const size_t poff = ((size_t)pg << a.log_page) * a.Hkv * D;
                 const __amdgpu_buffer_rsrc_t kp = make_rsrc((const uint16_t *)a.k + poff, rng);

@@ -3,8 +3,8 @@ fp64 oracle over every output row (needs an MI355X).
 
 The planner routes decode with 4 query rows per kv head at head dim 128 (GQA
 4, one query token) to the vector-ALU kernel with 4 rows and 8 kv heads per
-workgroup only when the contiguous caches hold at least 256 MiB; below that
-the matrix-core kernel's 16-row variant runs.  So these tests use caches of
+workgroup only when the caches (contiguous or paged) hold at least 256 MiB;
+below that the matrix-core kernel's 16-row variant runs.  So these tests use caches of
 at least that size, short ragged lengths (the route depends on capacity, not
 on lengths, and the oracle then finishes in seconds), both dtypes, the
 balanced schedule and forced partition counts, and assert the plan.  The
@@ -81,6 +81,23 @@ def test_valu_four_row_variant_library_scratch():
     print(parity.compare(out, lse, ref_o, ref_l, "bf16"), flush=True)
 
 
+@pytest.mark.parametrize("P", [16, 64, 256])
+def test_valu_four_row_variant_paged(P):
+    """The same route through a paged cache (the page lookups run a step
+    ahead of the loads), scattered into a random page order with poisoned
+    spare pages and out-of-pool block-table entries past each sequence."""
+    w = _headline_shape("bf16", 7400 + P, outliers=True)
+    inp = wl.make_inputs(w, lengths=HEADLINE_LENGTHS)
+    pg = wl.to_paged(inp, P)
+    out, lse, plan = parity.run_gpu_paged(pg, inp)
+    _assert_headline_plan(plan, 1)
+    ref_o, ref_l = oracle.attention(inp.q, inp.k_cache, inp.v_cache, inp.cache_seqlens,
+                                    w.causal, w.dtype)
+    rep = parity.compare(out, lse, ref_o, ref_l, w.dtype)
+    print(w.name, P, plan, rep, flush=True)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
 @pytest.mark.parametrize("name", wl.LONG_KV_NAMES)
 def test_long_kv_full_size_every_row(name):
     """The full-size batch in the benchmark's launch configuration (planner's
@@ -104,6 +121,8 @@ def test_paged_full_size_every_row(name, P):
     inp = wl.make_inputs(w)
     pg = wl.to_paged(inp, P)
     out, lse, plan = parity.run_gpu_paged(pg, inp)
+    if name != "llama70b_mtp_decode":
+        _assert_headline_plan(plan, 1)
     ref_o, ref_l = oracle.attention(inp.q, inp.k_cache, inp.v_cache, inp.cache_seqlens,
                                     w.causal, w.dtype)
     rep = parity.compare(out, lse, ref_o, ref_l, w.dtype)
