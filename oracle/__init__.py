@@ -25,11 +25,20 @@ FP16, BF16 = 0, 1
 
 
 def compile_oracle(out_path: str = LIB_PATH, mutant: int = 0) -> str:
-    """Compile oracle.c with gcc (OpenMP, -O2, IEEE semantics kept)."""
+    """Compile oracle.c with gcc (OpenMP, -O2, IEEE semantics kept).
+
+    The library is written under a temporary name and renamed into place, so
+    a process loading it (another test worker, say) never sees a partial file."""
+    tmp = f"{out_path}.{os.getpid()}.tmp"
     cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared",
            "-fno-fast-math", "-ffp-contract=off", f"-DMXO_MUTANT={int(mutant)}",
-           _SRC, "-o", out_path, "-lm"]
-    subprocess.run(cmd, check=True)
+           _SRC, "-o", tmp, "-lm"]
+    try:
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out_path)
+    finally:
+        if os.path.exists(tmp):
+            os.remove(tmp)
     return out_path
 
 
