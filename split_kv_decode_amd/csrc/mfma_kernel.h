@@ -251,8 +251,10 @@ struct Mfma {
             t_end = max(t_end, t_lo);   // an empty segment, never a negative range
         }
         t_end = __builtin_amdgcn_readfirstlane(t_end);
-        // first key of tile 0: a paged cache is read in page-aligned tiles
-        const int t_base = PAGED ? (t_lo & ~(kKT - 1)) : t_lo;
+        // first key of tile 0.  A paged cache is read in page-aligned tiles:
+        // its segments start on multiples of kKT (the schedule rounds their
+        // bounds), so no tile holds keys from before the segment.
+        const int t_base = t_lo;
         const int ntiles = t_end > t_lo ? (t_end - t_base + kKT - 1) / kKT : 0;
         const int my_tiles = ntiles > sub ? (ntiles - sub + WPH - 1) / WPH : 0;
 
@@ -325,43 +327,61 @@ struct Mfma {
                 pg[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
                     bt_rsrc, (uint32_t)((t0 + 16 * h) >> a.log_page) * 4u, 0, 0);
         };
-        // the load whose first key is tok, from page entry e, through a
-        // descriptor whose range ends at the last token below t_end
-        auto page_load = [&](const void *pool, uint32_t tokb, size_t row_elems, int tok,
-                             uint32_t e, uint32_t lane_off, int e0, int lim) {
-            const int pi = tok >> a.log_page;
-            const int valid = t_end - (pi << a.log_page);
-            const int pg = clampi(__builtin_amdgcn_readfirstlane((int)e), 0, a.num_pages - 1);
-            const uint32_t rng = valid <= 0 ? 0u : (uint32_t)min(valid, page) * tokb;
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(
-                (const uint16_t *)pool + ((size_t)pg << a.log_page) * row_elems, rng);
-            const uint32_t off = (uint32_t)(tok & (page - 1)) * tokb + lane_off;
-            if constexpr (ODD) return load_chunk_elems<POL>(r, off, e0, lim);
-            else return load16<POL>(r, off);
+        // a tile's two 16-key halves each lie in one page (the same page when
+        // pages hold 32 keys or more), and so does every load (its keys stay
+        // inside one half): per half one descriptor from the half's
+        // block-table entry, whose range ends at the last token below t_end,
+        // and the half's byte offset in that page.  Built once per tile and pool, so
+        // a load adds only its key's constant offset (a descriptor and a
+        // multiply per load cost about 200 scalar instructions and register
+        // spills per tile, 3-5 us on the Llama-70B-shaped MTP batch).
+        auto page_halves = [&](const void *pool, uint32_t tokb, size_t row_elems, int t0,
+                               __amdgpu_buffer_rsrc_t (&r)[2], uint32_t (&soff)[2]) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int th = t0 + 16 * h;
+                const int valid = t_end - (th & ~(page - 1));
+                const int pg = clampi(__builtin_amdgcn_readfirstlane((int)pg_cur[h]), 0,
+                                      a.num_pages - 1);
+                const uint32_t rng = valid <= 0 ? 0u : (uint32_t)min(valid, page) * tokb;
+                r[h] = make_rsrc((const uint16_t *)pool + ((size_t)pg << a.log_page) * row_elems,
+                                 rng);
+                soff[h] = (uint32_t)(th & (page - 1)) * tokb;
+            }
         };
         auto gload_v = [&](int j) {
-            const int t0 = PAGED ? t_base + j * kKT : t_lo + j * kKT;
+            const int t0 = t_base + j * kKT;
+            __amdgpu_buffer_rsrc_t pr[2];
+            uint32_t ps[2];
+            if constexpr (PAGED) page_halves(a.v, vtok, (size_t)a.Hkv * a.Dv, t0, pr, ps);
 #pragma unroll
             for (int u = 0; u < LDV; ++u) {
                 const int tok = t0 + 64 * u / NCHV;
-                if constexpr (PAGED)
-                    vs[u] = page_load(a.v, vtok, (size_t)a.Hkv * a.Dv, tok, pg_cur[tok - t0 >= 16],
-                                      voff[u], 8 * vch[u], a.Dv);
-                else if constexpr (ODD)
+                if constexpr (PAGED) {
+                    const int dt = 64 * u / NCHV, h = dt >= 16 ? 1 : 0;
+                    const uint32_t off = ps[h] + (uint32_t)(dt - 16 * h) * vtok + voff[u];
+                    if constexpr (ODD) vs[u] = load_chunk_elems<POL>(pr[h], off, 8 * vch[u], a.Dv);
+                    else vs[u] = load16<POL>(pr[h], off);
+                } else if constexpr (ODD)
                     vs[u] = load_chunk_elems<POL>(vrsrc, (uint32_t)tok * vtok + voff[u], 8 * vch[u], a.Dv);
                 else
                     vs[u] = load16<POL>(vrsrc, (uint32_t)tok * vtok + voff[u]);
             }
         };
         auto gload_k = [&](int j) {
-            const int t0 = PAGED ? t_base + j * kKT : t_lo + j * kKT;
+            const int t0 = t_base + j * kKT;
+            __amdgpu_buffer_rsrc_t pr[2];
+            uint32_t ps[2];
+            if constexpr (PAGED) page_halves(a.k, ktok, (size_t)a.Hkv * a.Dk, t0, pr, ps);
 #pragma unroll
             for (int u = 0; u < LDK; ++u) {
                 const int tok = KD ? t0 + 16 * (u / KK) : t0 + 64 * u / NCHK;
-                if constexpr (PAGED)
-                    ks[u] = page_load(a.k, ktok, (size_t)a.Hkv * a.Dk, tok, pg_cur[tok - t0 >= 16],
-                                      koff[u], 8 * kch[u], a.Dk);
-                else if constexpr (ODD)
+                if constexpr (PAGED) {
+                    const int dt = KD ? 16 * (u / KK) : 64 * u / NCHK, h = dt >= 16 ? 1 : 0;
+                    const uint32_t off = ps[h] + (uint32_t)(dt - 16 * h) * ktok + koff[u];
+                    if constexpr (ODD) ks[u] = load_chunk_elems<POL>(pr[h], off, 8 * kch[u], a.Dk);
+                    else ks[u] = load16<POL>(pr[h], off);
+                } else if constexpr (ODD)
                     ks[u] = load_chunk_elems<POL>(krsrc, (uint32_t)tok * ktok + koff[u], 8 * kch[u], a.Dk);
                 else
                     ks[u] = load16<POL>(krsrc, (uint32_t)tok * ktok + koff[u]);
@@ -424,8 +444,6 @@ struct Mfma {
 
         auto compute = [&](int set, int j, int jn, int jnn) {
             const int key0 = t_base + j * kKT;
-            // paged: keys of the first tile before t_lo are not part of the segment
-            const int vis_lo = (PAGED && key0 < t_lo) ? t_lo - key0 - 4 * g : INT32_MIN;
             // stage this tile's K (without KD) and V rows in the wave's LDS
             // buffer `set`; the next tile streams while this one is computed
             if constexpr (!KD) {
@@ -472,8 +490,7 @@ struct Mfma {
                         acc = T::mma(ka[kb][kk], qf[rt][kk], acc);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float v = (16 * kb + i <= vis && 16 * kb + i >= vis_lo)
-                                            ? acc[i] * a.qscale : kNegInf;
+                        const float v = 16 * kb + i <= vis ? acc[i] * a.qscale : kNegInf;
                         x[rt][kb][i] = v;
                         mloc[rt] = fmaxf(mloc[rt], v);
                     }
@@ -640,8 +657,10 @@ __attribute__((amdgpu_waves_per_eu(SMALL && !ODD ? 2 : 1, SMALL && !ODD ? 2 : 1)
 void split_kv_mfma_kernel(KernelArgs a) {
     using M = Mfma<DT, DK, DV, HPW, PAGED, POL, SMALL, KD, ODD>;
     __shared__ __attribute__((aligned(16))) typename M::Smem sm;
-    drive_schedule<SCHED>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi, int slot,
-                                 bool whole) {
+    // a paged cache is read in page-aligned tiles, so its segments start on
+    // tile boundaries (no key of a segment's first tile precedes it)
+    drive_schedule<SCHED, PAGED ? kKT : 1>(a, [&](int b, int n, int hb, int rb, int t_lo, int t_hi,
+                                                 int slot, bool whole) {
         M::segment(a, sm, b, n, hb, rb, t_lo, t_hi, slot, whole);
     });
 }

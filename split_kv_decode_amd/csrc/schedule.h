@@ -12,7 +12,12 @@
 //              ceil(total / P), min_share), as one segment per stream it
 //              touches, slot w + st.
 // `whole` marks a segment that is its stream's entire range; the kernel then
-// writes the final output instead of a partial.  The valid lengths live on
+// writes the final output instead of a partial.  With ALIGN > 1 every bound
+// inside a stream is rounded down to a multiple of ALIGN (the stream's end
+// stays n): neighbouring segments round their shared bound alike, so they
+// still cover [0, n) once, and a segment that rounds to nothing is still
+// handed over (its workgroup writes an empty partial to its slot, which the
+// merge kernel counts).  `whole` is decided on the bounds before rounding.  The valid lengths live on
 // the device, so in the balanced schedule every workgroup first forms their
 // prefix sums (workgroup 0 also stores them, and W, for the merge kernel).
 #pragma once
@@ -113,9 +118,10 @@ __device__ __forceinline__ void length_prefix_sums(const KernelArgs &a, long lon
     __syncthreads();
 }
 
-template <int SCHED, class Segment>
+template <int SCHED, int ALIGN = 1, class Segment>
 __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&segment) {
     const int HR = a.head_blocks * a.row_blocks;
+    auto bound = [](int t, int n) { return t >= n ? n : (t & ~(ALIGN - 1)); };
     if constexpr (SCHED == kFixed) {
         const int split = blockIdx.x;
         const int y = blockIdx.y;
@@ -125,7 +131,7 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         if (split > 0 && t_lo >= n) return;   // partition past this sequence
         const int t_hi = min(t_lo + a.chunk, n);
         const int slot = (b * HR + y) * a.S + split;
-        segment(b, n, y / a.row_blocks, y % a.row_blocks, t_lo, t_hi, slot,
+        segment(b, n, y / a.row_blocks, y % a.row_blocks, bound(t_lo, n), bound(t_hi, n), slot,
                 t_lo == 0 && t_hi == n);
     } else {
         __shared__ long long cum[kMaxBalancedBatch + 1];
@@ -171,8 +177,8 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         int t = uni((int)(off - (long long)j * n));
         while (g < gend) {
             const int seg = (int)((long long)(n - t) < gend - g ? (long long)(n - t) : gend - g);
-            segment(b, n, j / a.row_blocks, j % a.row_blocks, t, t + seg, (int)(w + b * HR + j),
-                    t == 0 && seg == n);
+            segment(b, n, j / a.row_blocks, j % a.row_blocks, bound(t, n), bound(t + seg, n),
+                    (int)(w + b * HR + j), t == 0 && seg == n);
             g += seg;
             t = 0;
             if (++j == HR) {
