@@ -78,6 +78,40 @@ def test_paged_forced_splits(path, num_splits):
     assert plan["schedule"] == 0 and plan["path"] == path
 
 
+@pytest.mark.parametrize("num_splits", [40, 64, 100, 777])
+@pytest.mark.parametrize("kind", ["mfma64rows", "mfma16rows", "valu"])
+def test_paged_partitions_shorter_than_a_tile(kind, num_splits):
+    """Forced partitions of 1-20 keys.  The matrix-core kernel reads a paged
+    cache in 32-key tiles and its segments start on tile boundaries: most of
+    these partitions round to nothing and write empty partials, the others
+    to whole tiles; the merge must count both.  The VALU kernel keeps its own
+    bounds (masked to the key)."""
+    if kind == "mfma64rows":
+        w = wl.Workload("tiny_parts", B=3, qLen=8, Hq=16, Hkv=2, D=128, kv_cap=777,
+                        dtype="bf16", causal=True, sigma=1.0, seed=61, len_range=(1, 777))
+    elif kind == "mfma16rows":
+        w = wl.Workload("tiny_parts", B=3, qLen=1, Hq=32, Hkv=4, D=64, kv_cap=777,
+                        dtype="fp16", causal=False, sigma=1.0, seed=62, len_range=(1, 777))
+    else:
+        w = wl.Workload("tiny_parts", B=3, qLen=1, Hq=8, Hkv=8, D=128, kv_cap=777,
+                        dtype="bf16", causal=False, sigma=1.0, seed=63, len_range=(1, 777))
+    inp = wl.make_inputs(w, lengths=[777, 45, 1])
+    _, _, plan = _check(inp, 16, num_splits=num_splits)
+    assert plan["schedule"] == 0 and plan["path"] == ("valu" if kind == "valu" else "mfma")
+
+
+@pytest.mark.parametrize("P", [16, 32, 64])
+def test_paged_balanced_shares_start_inside_tiles(P):
+    """Balanced shares of 64 keys laid over sequences whose lengths are not
+    multiples of 32, so share bounds fall inside tiles and are rounded (one
+    16-row tile per kv head: the matrix-core kernel's small variant)."""
+    w = wl.Workload("odd_shares", B=7, qLen=2, Hq=16, Hkv=2, D=128, kv_cap=1000, dtype="bf16",
+                    causal=True, sigma=1.0, seed=64 + P, len_range=(1, 1000))
+    inp = wl.make_inputs(w, lengths=[1000, 33, 999, 31, 65, 517, 2])
+    _, _, plan = _check(inp, P)
+    assert plan["schedule"] == 1 and plan["path"] == "mfma", plan
+
+
 def test_paged_library_scratch_and_whole_pages():
     # lengths at, just below and just above page boundaries; no caller workspace
     w = wl.Workload("edges", B=5, qLen=1, Hq=16, Hkv=4, D=128, kv_cap=512, dtype="fp16",
