@@ -118,6 +118,13 @@ __device__ __forceinline__ void length_prefix_sums(const KernelArgs &a, long lon
     __syncthreads();
 }
 
+// Tokens per workgroup share of the balanced schedule when the streams hold
+// T tokens in all (every workgroup and the merge kernel derive it alike).
+__device__ __forceinline__ long long balanced_share(const KernelArgs &a, long long T) {
+    const long long W = div_nn(T + a.S - 1, a.S);
+    return W < a.min_share ? (long long)a.min_share : W;
+}
+
 template <int SCHED, int ALIGN = 1, class Segment>
 __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&segment) {
     const int HR = a.head_blocks * a.row_blocks;
@@ -144,9 +151,7 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         if (!uniform) length_prefix_sums(a, cum, wave_tot);
         auto cumv = [&](int bb) -> long long { return uniform ? bb * n_u : cum[bb]; };
         const long long T = uni(cumv(a.B) * HR);
-        long long W = div_nn(T + a.S - 1, a.S);
-        if (W < a.min_share) W = a.min_share;
-        W = uni(W);
+        const long long W = uni(balanced_share(a, T));
         if (blockIdx.x == 0) {
             for (int bb = threadIdx.x; bb <= a.B; bb += kScheduleThreads)
                 ((long long *)a.ws_cum)[bb] = cumv(bb);
