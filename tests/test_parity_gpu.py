@@ -207,15 +207,25 @@ def test_out_of_range_seqlens_are_clamped():
     parity.compare(out, lse, ref_o, ref_l, "fp16")
 
 
-def test_fp16_large_scores_do_not_overflow():
-    """Scores far beyond the fp16 range (|s| ~ 1e4) must stay finite."""
-    g = torch.Generator().manual_seed(31)
-    w = wl.Workload("ovf", B=1, qLen=2, Hq=4, Hkv=1, D=128, kv_cap=300, dtype="fp16",
+@pytest.mark.parametrize("qLen,Hq,Hkv,D,path,rb", [
+    (1, 4, 4, 128, "valu", 1),      # one row per kv head
+    (1, 8, 4, 128, "valu", 2),      # two rows
+    (2, 4, 1, 128, "mfma", 16),     # the 16-row matrix-core tiles
+    (4, 16, 1, 128, "mfma", 64),    # the 64-row tiles
+    (1, 4, 1, 100, "mfma", 16),     # a head dim that is not a multiple of 8
+])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_fp16_large_scores_do_not_overflow(qLen, Hq, Hkv, D, path, rb, num_splits):
+    """Scores far beyond the fp16 range (|s| ~ 1e4) must stay finite, on every
+    kernel variant and through the merge of partitions."""
+    g = torch.Generator().manual_seed(31 + D + Hq)
+    w = wl.Workload("ovf", B=1, qLen=qLen, Hq=Hq, Hkv=Hkv, D=D, kv_cap=300, dtype="fp16",
                     causal=True, sigma=1.0, seed=31)
     inp = wl.make_inputs(w)
-    inp.q = (torch.randn(1, 2, 4, 128, generator=g) * 200).to(torch.float16)
-    inp.k_cache = (torch.randn(1, 300, 1, 128, generator=g) * 200).to(torch.float16)
-    out, lse, _ = parity.run_gpu(inp)
+    inp.q = (torch.randn(1, qLen, Hq, D, generator=g) * 200).to(torch.float16)
+    inp.k_cache = (torch.randn(1, 300, Hkv, D, generator=g) * 200).to(torch.float16)
+    out, lse, plan = parity.run_gpu(inp, num_splits)
+    assert (plan["path"], plan["row_block"]) == (path, rb), plan
     ref_o, ref_l = parity.oracle_full(inp)
     assert np.abs(ref_l).max() > 1e4
     parity.compare(out, lse, ref_o, ref_l, "fp16", lse_rel=2 ** -22)
