@@ -65,12 +65,42 @@ SPLIT_KERNEL = {"valu": "split_kv_valu_kernel", "mfma": "split_kv_mfma_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def code_text(src: str) -> str:
+    """C/C++ source without its comments, blank lines and runs of spaces:
+    what the compiler sees, so that an edit of comments or layout leaves a
+    kernel's digest (and the counters recorded against it) valid.  String
+    and character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c == "/" and src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif c == "/" and src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    lines = (" ".join(line.split()) for line in "".join(out).splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_digest(kernel: str) -> str:
-    """Digest of the sources `kernel` is built and planned from."""
+    """Digest of the code (comments and layout left out) of the sources
+    `kernel` is built and planned from."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 
