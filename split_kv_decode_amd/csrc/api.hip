@@ -135,9 +135,16 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 // Slot layout of the VALU kernel: whole head groups when Hkv allows it, so
 // that a workgroup streams whole token rows of the cache (all heads side by
 // side), else one head per workgroup.
-int valu_layout(int Hkv, int D, int *heads_per_block) {
+// Slot layout of the VALU kernel.  Whole token rows (2 * tpw heads, the
+// slots of both wave pairs) stream best on large caches; below 256 MiB of
+// K/V (small: true) half that block doubles the streams, so that the share
+// floor leaves no workgroup idle on short caches and each output row has
+// half the partials to merge: SmallQ MHA q1/q2 calls (32 heads, 1K-4K keys)
+// took 12.2-18.7 against 13.7-19.8 us per call (one head per workgroup was
+// slower from 3K keys on).
+int valu_layout(int Hkv, int D, bool small, int *heads_per_block) {
     const int tpw = 64 / (D / 8);
-    if (Hkv % (2 * tpw) == 0) {
+    if (!small && Hkv % (2 * tpw) == 0) {
         *heads_per_block = 2 * tpw;
         return kHeadsX2;
     }
@@ -233,7 +240,7 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     } else {
         pl.path = MXFA_PATH_VALU;
         pl.row_block = next_pow2_le8((int)R);
-        pl.layout = valu_layout(p.Hkv, p.D, &hpb);
+        pl.layout = valu_layout(p.Hkv, p.D, cache_bytes < kValuStreamBytes, &hpb);
     }
     const int row_blocks = R > 0 ? ceil_div(R, pl.row_block) : 1;
     pl.head_block = hpb;

@@ -193,6 +193,8 @@ constexpr int kMfmaMinRows128 = 4;
 // step's block-table entry a step ahead: over 16-256 token pages the Qwen3-8B
 // batch reached 84.5-84.7% of HBM peak against 80.5-80.9% on the matrix-core
 // kernel, the Qwen3-4B long batch 79.7-80.0% against 76.2-77.3%.
+// Below the same size the VALU kernel's workgroups take half a token row's
+// heads (valu_layout in api.hip).
 constexpr unsigned long long kValuStreamBytes = 256ull << 20;
 // At most 16 rows per kv head (e.g. GQA 8 with one query token): the
 // matrix-core kernel's small variant, one 16-row tile per wave and two

@@ -434,6 +434,22 @@ def test_four_rows_take_the_valu_kernel_on_large_caches():
     assert m.plan(4, 64, 8, 128, 8, 32768, 1, 1, 0, 80).grid_x == 80
 
 
+def test_valu_head_blocks_follow_the_cache_size():
+    # below 256 MiB of K/V: half a token row's heads per workgroup (4 at
+    # head dim 128, 8 at 64); from 256 MiB on: the whole row (8, 16)
+    for D, small_hb, big_hb in ((128, 4, 8), (64, 8, 16)):
+        p = m.plan(1, 32, 32, D, 1, 4096, 0, 0, 0, 256)           # 8-16 MiB
+        assert (p.path, p.head_block, p.layout) == (0, small_hb, 1)
+        p = m.plan(1, 64, 32, D, 1, 4096, 0, 0, 0, 256)           # two rows
+        assert (p.path, p.row_block, p.head_block, p.layout) == (0, 2, small_hb, 1)
+        unit = 16 * 16 * 2 * D * 2                                 # bytes per token of capacity
+        cap = -(-(256 << 20) // unit)                              # the first at 256 MiB or more
+        p = m.plan(16, 16, 16, D, 1, cap, 0, 1, 0, 256)
+        assert (p.path, p.head_block, p.layout) == (0, big_hb, 0)
+        p = m.plan(16, 16, 16, D, 1, cap - 1, 0, 1, 0, 256)       # just under
+        assert (p.path, p.head_block, p.layout) == (0, small_hb, 1)
+
+
 def test_plan_fills_the_chip_at_low_batch():
     p = m.plan(1, 32, 32, 128, 1, 4096, 0, 0, 0, 256)
     assert p.grid_x * p.grid_y * p.grid_z >= 256       # at least one workgroup per CU

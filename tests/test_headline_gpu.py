@@ -98,6 +98,30 @@ def test_valu_four_row_variant_paged(P):
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
 
+@pytest.mark.parametrize("rows", [1, 2])
+@pytest.mark.parametrize("dtype,num_splits,paged", [("bf16", 0, False), ("fp16", 0, False),
+                                                    ("bf16", 5, False), ("fp16", 0, True)])
+def test_valu_whole_row_variants_every_row(rows, dtype, num_splits, paged):
+    """One and two query rows per kv head on caches of 256 MiB and more run the
+    VALU kernel with 8 kv heads per workgroup (whole 2 KiB token rows); below
+    that size the planner takes 4.  16 kv heads, 8 x 8192 tokens: 512 MiB."""
+    w = wl.Workload("valu_rows", B=8, qLen=1, Hq=16 * rows, Hkv=16, D=128, kv_cap=8192,
+                    dtype=dtype, causal=False, sigma=1.0, seed=7500 + 10 * rows + num_splits,
+                    len_range=(0, 8192))
+    inp = wl.make_inputs(w, lengths=[3000, 0, 1, 8192, 17, 513, 64, 2])
+    if paged:
+        out, lse, plan = parity.run_gpu_paged(wl.to_paged(inp, 64), inp)
+    else:
+        out, lse, plan = parity.run_gpu(inp, num_splits)
+    assert plan["path"] == "valu" and plan["head_block"] == 8 and plan["layout"] == 0, plan
+    assert plan["row_block"] == rows, plan
+    ref_o, ref_l = oracle.attention(inp.q, inp.k_cache, inp.v_cache, inp.cache_seqlens,
+                                    w.causal, w.dtype)
+    rep = parity.compare(out, lse, ref_o, ref_l, dtype)
+    print(w.name, rows, dtype, num_splits, paged, plan, rep, flush=True)
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
 @pytest.mark.parametrize("name", wl.LONG_KV_NAMES)
 def test_long_kv_full_size_every_row(name):
     """The full-size batch in the benchmark's launch configuration (planner's
