@@ -1,5 +1,6 @@
 """Seeded random configurations on the GPU vs the fp64 oracle (needs an
-MI355X).
+MI355X).  A second, wider draw (up to 32 kv heads, any head dim, longer
+caches) adds 200 cases.
 
 Each case draws a shape (batch, query length, GQA group, kv heads, head dim
 64 or 128, dtype, causal mask, capacity), ragged lengths including empty
@@ -153,3 +154,45 @@ def test_random_in_call_append(case):
     print(f"case {case}: {w.describe()} lens={lens} new_len={new_len} page={P}", flush=True)
     inp = wl.make_inputs(w, lengths=lens)
     parity.run_append(inp, new_len, P, num_splits=int(r.choice([0, 0, 2])), seed=case)
+
+
+def draw_wide(case):
+    """A wider space: up to 32 kv heads (every VALU slot layout, caches from a
+    few KB to ~0.5 GB), head dims 64, 128 or any in 1..256, 16-token query
+    drafts, caches up to 5000 keys, page sizes up to 256."""
+    r = np.random.default_rng([SEED + 1, case])
+    B = int(r.integers(1, 7))
+    qLen = int(r.choice([1, 1, 1, 2, 3, 4, 8, 16]))
+    G = int(r.choice([1, 2, 4, 8]))
+    Hkv = int(r.choice([1, 2, 3, 4, 8, 12, 16, 32]))
+    D = int(r.choice([64, 128, 128, int(r.integers(1, 257))]))
+    dtype = str(r.choice(["fp16", "bf16"]))
+    causal = bool(r.integers(0, 2))
+    cap = int(r.choice([int(r.integers(1, 600)), int(r.integers(600, 5000))]))
+    lengths = [int(x) for x in r.integers(0, cap + 1, size=B)]
+    if r.random() < 0.3:
+        lengths[int(r.integers(0, B))] = cap
+    num_splits = int(r.choice([0, 0, 0, 1, 2, 5, 33]))
+    page = int(r.choice([0, 0, 16, 64, 256]))
+    G = min(G, max(1, 64 // Hkv))
+    w = wl.Workload(f"wide{case}", B=B, qLen=qLen, Hq=G * Hkv, Hkv=Hkv, D=D, kv_cap=cap,
+                    dtype=dtype, causal=causal, sigma=float(r.choice([0.5, 1.0])),
+                    seed=SEED + 7000 + case, len_range=(0, cap))
+    return w, lengths, num_splits, page
+
+
+@pytest.mark.parametrize("case", range(200))
+def test_random_wide_configuration(case):
+    w, lengths, num_splits, page = draw_wide(case)
+    inp = wl.make_inputs(w, lengths=lengths)
+    print(f"case {case}: {w.describe()} lengths={lengths} splits={num_splits} page={page}",
+          flush=True)
+    if page:
+        pg = wl.to_paged(inp, page, seed=case)
+        out, lse, plan = parity.run_gpu_paged(pg, inp, num_splits)
+        ref_o, ref_l = parity.oracle_paged(pg, inp)
+    else:
+        out, lse, plan = parity.run_gpu(inp, num_splits)
+        ref_o, ref_l = parity.oracle_full(inp)
+    rep = parity.compare(out, lse, ref_o, ref_l, w.dtype)
+    print(case, plan, rep, flush=True)
