@@ -91,6 +91,15 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it first "
                            "(python split_kv_decode_amd/build.py)")
+    # torch ships its own HIP runtime, and a process holds one copy of it:
+    # libamdhip64.so.7 is resolved by its soname to whichever copy is loaded
+    # first.  Loading this library before torch would install the system
+    # copy, and torch would then find no GPU; importing torch first makes its
+    # copy the one this library calls (as the tensors it is given require).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.mxfa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 8 + [vp]

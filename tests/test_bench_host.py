@@ -38,3 +38,23 @@ def test_every_kernel_has_a_digest():
     for kernel in bench.KERNEL_SOURCES:
         d = bench.kernel_digest(kernel)
         assert len(d) == 16 and int(d, 16) >= 0
+
+
+def test_library_binds_to_the_hip_runtime_torch_brings():
+    """Loading the library first (before anything imported torch) must still
+    leave torch's own HIP runtime as the process's one copy."""
+    import os
+    import subprocess
+    import sys
+    code = ("import split_kv_decode_amd as mx; mx.lib(); import torch, os; "
+            "maps = open('/proc/self/maps').read().split('\\n'); "
+            "paths = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}); "
+            "print('\\n'.join(paths))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True,
+                         text=True, timeout=600)
+    assert out.returncode == 0, out.stderr
+    paths = [p for p in out.stdout.split("\n") if p]
+    import torch
+    torch_lib = os.path.join(os.path.dirname(torch.__file__), "lib")
+    assert len(paths) == 1 and paths[0].startswith(torch_lib), paths
