@@ -95,3 +95,4 @@ def test_captured_call_replays(kind, w, noalloc):
         rep_ = parity.compare(parity.to_f64(got_o), got_l.cpu().double().numpy(), ro, rl,
                               w.dtype)
         print(kind, noalloc, rep, plan["path"], rep_, flush=True)
+
