@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(KernelArgs a) {
     const int wave = threadIdx.x >> 6;
     const int sub = wave % WPR;                 // this wave's share of the partials
     // rows in XCD order (schedule.h): a row is merged on the XCD whose
-    // workgroups wrote most of its partials
+    // workgroups wrote most of its partials (its reads still miss that XCD's
+    // L2, which the split kernel's end has written back)
     const long long row = (long long)xcd_order(blockIdx.x, gridDim.x) * RPB + wave / WPR;
     const long long nrows = (long long)a.B * a.Hq * a.qLen;
     if (row >= nrows) return;                   // whole wave exits together
