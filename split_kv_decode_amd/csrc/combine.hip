@@ -80,19 +80,25 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(KernelArgs a) {
         // the prefix sums and the share size the split kernel used; without
         // per-sequence lengths every sequence holds n keys and both follow
         // directly, with no load of what the split kernel stored
-        long long cb, W;
-        if (a.seqlens == nullptr && a.cu_k == nullptr) {
-            cb = (long long)b * n;
-            W = balanced_share(a, (long long)a.B * n * HR);
+        const bool uniform = a.seqlens == nullptr && a.cu_k == nullptr;
+        if (uniform && a.uni_spw > 0) {
+            count = a.uni_spw;                  // shares st * spw + i, slots + st
+            first = (long long)st * (a.uni_spw + 1);
         } else {
-            const long long *cw = (const long long *)a.ws_cum;
-            cb = cw[b];
-            W = cw[a.B + 1];
+            long long cb, W;
+            if (uniform) {
+                cb = (long long)b * n;
+                W = a.uni_w;
+            } else {
+                const long long *cw = (const long long *)a.ws_cum;
+                cb = cw[b];
+                W = cw[a.B + 1];
+            }
+            const long long c0 = cb * HR + (long long)jst * n;   // stream start
+            const long long w_lo = c0 / W, w_hi = (c0 + n - 1) / W;
+            count = (int)(w_hi - w_lo + 1);
+            first = w_lo + st;
         }
-        const long long c0 = cb * HR + (long long)jst * n;   // stream start
-        const long long w_lo = c0 / W, w_hi = (c0 + n - 1) / W;
-        count = (int)(w_hi - w_lo + 1);
-        first = w_lo + st;
     } else {
         count = 0;
         first = 0;

@@ -67,6 +67,10 @@ struct KernelArgs {
     int chunk;                // kFixed: tokens per partition
     int S;                    // kFixed: partitions per stream; kBalanced: workgroups P
     int min_share;            // kBalanced: lower bound on tokens per workgroup
+    // kBalanced with sequences of one length (no seqlens, no cu_k), set on
+    // the host: tokens per workgroup share, and shares per stream when each
+    // stream gets shares of its own (0: the streams are concatenated)
+    int uni_w, uni_spw;
     float qscale;             // log2(e) / sqrt(D)
 };
 

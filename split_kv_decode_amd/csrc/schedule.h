@@ -10,7 +10,9 @@
 //              (in XCD order, see xcd_order) takes [w * W, (w + 1) * W) of
 //              the concatenation, W = max(
 //              ceil(total / P), min_share), as one segment per stream it
-//              touches, slot w + st.
+//              touches, slot w + st.  Without per-sequence lengths the
+//              host fixes W (uni_w) and may give every stream shares of its
+//              own (uni_spw per stream; see uniform_shares in api.hip).
 // `whole` marks a segment that is its stream's entire range; the kernel then
 // writes the final output instead of a partial.  With ALIGN > 1 every bound
 // inside a stream is rounded down to a multiple of ALIGN (the stream's end
@@ -149,9 +151,15 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         const bool uniform = a.seqlens == nullptr && a.cu_k == nullptr;
         const long long n_u = uniform ? seq_len_from(a, 0, 0) : 0;
         if (!uniform) length_prefix_sums(a, cum, wave_tot);
-        auto cumv = [&](int bb) -> long long { return uniform ? bb * n_u : cum[bb]; };
+        // L: the stride of one stream in the concatenation.  With lengths of
+        // one value the host has chosen the share width (uni_w) and, when
+        // every stream gets shares of its own (uni_spw > 0), each stream is
+        // padded to whole shares (L = uni_spw * W); segments end at the
+        // stream's real length
+        const long long L = uniform && a.uni_spw > 0 ? (long long)a.uni_spw * a.uni_w : n_u;
+        auto cumv = [&](int bb) -> long long { return uniform ? bb * L : cum[bb]; };
         const long long T = uni(cumv(a.B) * HR);
-        const long long W = uni(balanced_share(a, T));
+        const long long W = uni(uniform ? (long long)a.uni_w : balanced_share(a, T));
         if (blockIdx.x == 0) {
             for (int bb = threadIdx.x; bb <= a.B; bb += kScheduleThreads)
                 ((long long *)a.ws_cum)[bb] = cumv(bb);
@@ -165,10 +173,10 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
         if (g >= T) return;
         const long long gend = g + W < T ? g + W : T;
         // sequence holding global token g: the last b with cum[b] * HR <= g
-        // (g < T, so with uniform lengths n_u > 0)
+        // (g < T, so with uniform lengths L > 0)
         int lo = 0, hi = a.B - 1;
         if (uniform) {
-            lo = (int)div_nn(g, n_u * HR);
+            lo = (int)div_nn(g, L * HR);
         } else {
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
@@ -176,14 +184,17 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
             }
         }
         int b = uni(lo);
-        int n = uni((int)(cumv(b + 1) - cumv(b)));
+        int n = uni((int)(cumv(b + 1) - cumv(b)));      // stride of b's streams
+        const int nr = uniform ? (int)n_u : 0;           // real length (uniform)
         const long long off = uni(g - cumv(b) * HR);
         int j = uni((int)div_nn(off, n));
         int t = uni((int)(off - (long long)j * n));
         while (g < gend) {
             const int seg = (int)((long long)(n - t) < gend - g ? (long long)(n - t) : gend - g);
-            segment(b, n, j / a.row_blocks, j % a.row_blocks, bound(t, n), bound(t + seg, n),
-                    (int)(w + b * HR + j), t == 0 && seg == n);
+            const int len = uniform ? nr : n;
+            const int e = t + seg < len ? t + seg : len;
+            segment(b, len, j / a.row_blocks, j % a.row_blocks, bound(t, len), bound(e, len),
+                    (int)(w + b * HR + j), t == 0 && e == len);
             g += seg;
             t = 0;
             if (++j == HR) {
