@@ -346,8 +346,8 @@ mxfa_status device_cus(int *cus) {
 // streams (else *spw = 0 and the streams stay concatenated).  A straddling
 // workgroup runs two segments, each with its own start-up and partial
 // stores, and on short launches it is the last to finish: the SmallQ MHA
-// calls at 1023 and 3000 keys took 0.5-3.0 us less each (q4 kv1023 16.2 ->
-// 13.2 us, q8 kv3000 20.7 -> 18.3 us).
+// calls at 1023 and 3000 keys took 1.4-4.0 us less each (q4 kv1023 16.2 ->
+// 12.3 us, q8 kv3000 20.7 -> 17.1 us).
 void uniform_shares(long long n, long long N, int S, int min_share, int *w, int *spw) {
     const long long wc = (N * n + S - 1) / S;
     *w = (int)(wc < min_share ? min_share : wc);
