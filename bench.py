@@ -638,6 +638,10 @@ def other_configs(headline, args, torch, np, mx, wl, dev):
         m = measure_decode(w, CONFIG_STEPS, CONFIG_WARMUP, 0, 0, 0, torch, np, mx, wl, dev,
                            not args.no_dispatch_check)
         gbs = m["gbs"]
+        ceil_gbs = None
+        if not args.no_read_ceiling:
+            c = read_ceiling(torch, mx, dev, m["stream"], m["kv"], full=False)
+            ceil_gbs = c.get("nt_gbs_at_workload_size")
         recs.append({
             "workload": name, "B": w.B, "qLen": w.qLen, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
             "kv_cap": w.kv_cap, "sum_kv_len": int(sum(m["lens"])), "dtype": w.dtype,
@@ -650,7 +654,11 @@ def other_configs(headline, args, torch, np, mx, wl, dev):
             "path": m["plan"]["path"], "combine": m["plan"]["combine"],
             "split": {"kernel": m["kernel"], "mean_launch_us": round(m["split_ms_mean"] * 1e3, 2),
                       "gb_per_s": round(m["split_gbs"], 1),
-                      "frac": round(m["split_gbs"] / HBM_PEAK_GBS, 4)},
+                      "frac": round(m["split_gbs"] / HBM_PEAK_GBS, 4),
+                      # the read probe over reads of this workload's K/V size
+                      "size_matched_ceiling_gbs": ceil_gbs,
+                      "frac_of_size_matched_ceiling": (round(m["split_gbs"] / ceil_gbs, 4)
+                                                       if ceil_gbs else None)},
             "mfma_util": m["mfma_util"], "dispatch_check": m["dispatch"]})
         print(f"# {name}: {recs[-1]['wall_us_per_call']} us/call, "
               f"{recs[-1]['pct_of_hbm_peak']}% of peak", file=sys.stderr, flush=True)
@@ -664,13 +672,14 @@ MAX_COPIES = 64
 READ_PROBE_BYTES = 1 << 31
 
 
-def read_ceiling(torch, mx, dev, stream, size_bytes=0, reps=10):
+def read_ceiling(torch, mx, dev, stream, size_bytes=0, reps=10, full=True):
     """Median rate of the library's streaming-read probe over 2 GiB, with the
-    attention kernels' nt load policy and with the default policy; and, when
-    size_bytes is given (the workload's K/V bytes), with the nt policy over
-    reads of that size taken from consecutive windows of the 2 GiB buffer (so
-    that no read finds its bytes in the last-level cache): the ceiling at the
-    workload's own size, where the ramp and tail of one pass weigh more."""
+    attention kernels' nt load policy and with the default policy (full=True);
+    and, when size_bytes is given (the workload's K/V bytes), with the nt
+    policy over reads of that size taken from consecutive windows of the 2 GiB
+    buffer (so that no read finds its bytes in the last-level cache): the
+    ceiling at the workload's own size, where the ramp and tail of one pass
+    weigh more."""
     src = torch.ones(READ_PROBE_BYTES, dtype=torch.uint8, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -688,7 +697,7 @@ def read_ceiling(torch, mx, dev, stream, size_bytes=0, reps=10):
         torch.cuda.synchronize()
         return statistics.median(a.elapsed_time(b) for a, b in evs)
 
-    for nt in (True, False):
+    for nt in ((True, False) if full else ()):
         ms = median_ms([src], nt)
         out["nt_gbs" if nt else "default_gbs"] = round(READ_PROBE_BYTES / (ms * 1e-3) / 1e9, 1)
     size = min(int(size_bytes) // 16 * 16, READ_PROBE_BYTES)
