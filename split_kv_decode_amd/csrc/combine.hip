@@ -214,8 +214,14 @@ hipError_t launch_t(const KernelArgs &a, hipStream_t stream) {
         if (most < busy) busy = most;
     }
     const long long most_per_row = a.schedule == kFixed ? a.S : busy / (streams > 0 ? streams : 1) + 1;
-    // the grid-based count also decides when few rows need more workgroups
-    const bool wide = per_row > 24;
+    // the grid-based count also decides when few rows need more workgroups:
+    // one workgroup per row above 24 partials, or above 12 when there are at
+    // most 1024 rows (the Qwen3-4B-shaped batch, 512 rows of 17 partials:
+    // 156.0 against 156.4 us per call; the Llama-70B MTP batch, 2048 rows of
+    // 17, keeps one wave per row: 96.1 against 98.7 us; the exact count of
+    // stream-aligned shares, 16 for SmallQ q8 kv1023, measured 0.5 us slower
+    // than this estimate's choice of one workgroup per row there)
+    const bool wide = per_row > 24 || (per_row > 12 && nrows <= 1024);
     const int rpb = wide ? 1 : kWaves;
     const unsigned blocks = (unsigned)((nrows + rpb - 1) / rpb);
     const void *fn = !wide               ? (const void *)&combine_kernel<DT, D, 1, false>
