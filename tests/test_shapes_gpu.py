@@ -1,0 +1,68 @@
+"""Head-group and batch shapes at the edges of the planner (needs an MI355X).
+
+Grouped-query groups larger than 8 (multi-query attention with one kv head
+and 64 or 128 query heads; 16, 24 or 32 query heads per kv head), where a kv
+head carries up to 512 query rows, split into several 64-row blocks with a
+ragged last block, or fit one 16-row tile; and batches on both sides of the
+1024-sequence limit of the balanced schedule (more sequences take fixed
+partitions).  Every row is compared with the fp64 oracle.
+"""
+import pytest
+import torch
+
+import oracle
+import parity
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the -m gpu tests need an MI355X")
+    import split_kv_decode_amd as mx
+    mx.lib()
+    oracle.build()
+
+
+GROUPS = [
+    # (name, B, qLen, Hq, Hkv, D, kv_cap, dtype, causal)
+    ("mqa64_q1", 3, 1, 64, 1, 128, 2000, "bf16", False),       # 64 rows: one 64-row block
+    ("mqa128_q2", 2, 2, 128, 1, 128, 1500, "fp16", True),      # 256 rows: 4 blocks
+    ("mqa32_q8_d64", 2, 8, 32, 1, 64, 1200, "bf16", True),     # 256 rows at head dim 64
+    ("g16_q1", 4, 1, 32, 2, 128, 1800, "fp16", False),         # 16 rows: one 16-row tile
+    ("g24_q3", 2, 3, 96, 4, 128, 900, "bf16", True),           # 72 rows: a ragged second block
+    ("g32_q4_d96", 2, 4, 64, 2, 96, 700, "fp16", True),        # 128 rows, padded head dim
+    ("mqa128_q4", 1, 4, 128, 1, 128, 3000, "bf16", True),      # 512 rows: 8 blocks
+]
+
+
+@pytest.mark.parametrize("forced", [0, 4], ids=["planned", "forced4"])
+@pytest.mark.parametrize("case", GROUPS, ids=[c[0] for c in GROUPS])
+def test_large_query_head_groups(case, forced):
+    name, B, qLen, Hq, Hkv, D, cap, dtype, causal = case
+    w = wl.Workload(name, B=B, qLen=qLen, Hq=Hq, Hkv=Hkv, D=D, kv_cap=cap, dtype=dtype,
+                    causal=causal, sigma=1.0, seed=Hq + qLen + D, len_range=(0, cap))
+    lengths = [cap] + [int(x) for x in torch.randint(0, cap + 1, (B - 1,),
+                                                      generator=torch.Generator().manual_seed(B))]
+    inp = wl.make_inputs(w, lengths=lengths)
+    print(f"case {name} forced={forced} lengths={lengths}", flush=True)
+    out, lse, plan = parity.run_gpu(inp, num_splits=forced)
+    assert plan["path"] == "mfma" and plan["rows"] == Hq // Hkv * qLen, plan
+    ref_o, ref_l = parity.oracle_full(inp)
+    print(name, forced, plan, parity.compare(out, lse, ref_o, ref_l, dtype), flush=True)
+
+
+@pytest.mark.parametrize("B,schedule", [(1024, 1), (1025, 0), (1500, 0)])
+@pytest.mark.parametrize("qLen,Hq,Hkv,cap", [(1, 8, 8, 96), (4, 8, 2, 600)],
+                         ids=["valu", "mfma"])
+def test_batches_around_the_balanced_limit(B, schedule, qLen, Hq, Hkv, cap):
+    w = wl.Workload(f"b{B}", B=B, qLen=qLen, Hq=Hq, Hkv=Hkv, D=64, kv_cap=cap, dtype="bf16",
+                    causal=True, sigma=1.0, seed=B + qLen, len_range=(0, cap))
+    inp = wl.make_inputs(w)
+    print(f"case B={B} qLen={qLen} Hq={Hq} Hkv={Hkv}", flush=True)
+    out, lse, plan = parity.run_gpu(inp)
+    assert plan["schedule"] == schedule, plan
+    ref_o, ref_l = parity.oracle_full(inp)
+    print(B, plan, parity.compare(out, lse, ref_o, ref_l, "bf16"), flush=True)
