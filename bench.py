@@ -124,13 +124,16 @@ def _kernel_rows(csv_path):
         return list(csv.DictReader(f))
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma_dir=None):
+def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma_dir=None,
+                       page_size=0):
     """Turn rocprofv3 outputs (kernel-trace stats, FETCH_SIZE pass, WRITE_SIZE
     pass, each of a bench run with --copy-calibration, and for the matrix-core
     kernel a MfmaUtil / MfmaFlopsBF16 / MfmaFlopsF16 pass) into a short
     summary under profiles/ and the per-launch traffic record bench.py
     reports.  The traffic counters are scaled by what they read for the 1 GiB
-    device copy."""
+    device copy.  With page_size P the run read a paged cache: the record is
+    the workload's paged one (NAME_pagedP) and the algorithmic bytes add one
+    block-table entry per page touched."""
     import statistics
     stats = _kernel_rows(os.path.join(trace_dir, "run_kernel_stats.csv"))
     fetch = _kernel_rows(os.path.join(fetch_dir, "run_counter_collection.csv"))
@@ -160,10 +163,14 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma
     w = wl.WORKLOADS[workload]
     lens = wl.make_inputs(w).lengths() if w.len_range else [w.kv_cap] * w.B
     alg = wl.kv_bytes(w, lens) + w.B * w.qLen * w.Hq * w.D * w.elt
+    if page_size:
+        alg += sum(-(-max(0, min(n, w.kv_cap)) // page_size) for n in lens) * 4
+        workload = f"{workload}_paged{page_size}"
     kname = "split_kv_mfma_kernel" if "mfma" in split else "split_kv_valu_kernel"
     trace_rows = [r for r in stats if "split_kv_" in r["Name"] or "combine_kernel" in r["Name"]]
     lines = [f"# {kname} on {workload}", "",
-             f"Workload: {w.describe()}.", "",
+             f"Workload: {w.describe()}"
+             f"{f', K/V in pages of {page_size} tokens' if page_size else ''}.", "",
              "Commands (run from the repository root on one MI355X, after "
              "`cd /tmp && export TMPDIR=/tmp`):", ""]
     lines += [f"    {c}" for c in commands]
@@ -378,7 +385,7 @@ def main():
         if len(d) not in (3, 4):
             sys.exit("--summarize-profiles takes TRACE FETCH WRITE [MFMA]")
         summarize_profiles(d[0], d[1], d[2], args.workload, args.profile_command,
-                           d[3] if len(d) == 4 else None)
+                           d[3] if len(d) == 4 else None, args.page_size)
         return
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
