@@ -190,7 +190,12 @@ struct FullPlan {
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *fp) {
+// The partitioning of a problem whose kernel, tile (row block) and head
+// block are chosen (pl.path, pl.row_block, pl.layout, pl.rows set): fixed
+// partitions or the balanced schedule, the grid and the scratch layout.
+// *busy: how many workgroups get work when every sequence holds kv_cap keys.
+mxfa_status finish_plan(const Problem &p, long long R, bool odd, int num_splits, int num_cus,
+                        mxfa_plan_t pl, int hpb, FullPlan *fp, long long *busy) {
     constexpr int kChunkAlign = 64;
     constexpr int kTargetPerCU = 8;
     // workgroups per CU in the balanced grid: for the VALU kernel one (1-7%
@@ -202,46 +207,6 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     // variant, one for its 64-row tiles (their LDS and registers fill the CU)
     const int kValuPerCU = 1;
     constexpr int kMfmaPerCU = 1;
-    mxfa_plan_t pl;
-    std::memset(&pl, 0, sizeof(pl));
-    if (num_cus <= 0) num_cus = kDefaultCUs;
-    const int G = p.Hq / p.Hkv;
-    const long long R = (long long)G * p.qLen;
-    if (R > INT32_MAX) return MXFA_ERR_UNSUPPORTED;
-    pl.rows = (int)R;
-    int hpb = 1;
-    const bool valu_dims = p.dk() == p.dv() && (p.dk() == 64 || p.dk() == 128);
-    const int mfma_min = p.dk() == 128 ? kMfmaMinRows128 : kMfmaMinRows;
-    // at exactly the 128-dim threshold, large caches (contiguous or paged)
-    // stream faster through the VALU kernel (launch.h records the crossover)
-    const uint64_t cache_bytes =
-        (uint64_t)p.B * (uint64_t)p.kv_cap * p.Hkv * (uint64_t)(p.dk() + p.dv()) * 2;
-    const bool valu_stream = p.dk() == 128 && R == kMfmaMinRows128 &&
-                             cache_bytes >= kValuStreamBytes;
-    // head dims that are not multiples of 8: 2-byte aligned rows, element
-    // loads on the matrix-core kernel's 16-row tiles, one kv head per workgroup
-    const bool odd = odd_head_dims(p.dk(), p.dv());
-    if ((R >= mfma_min && !valu_stream) || !valu_dims) {
-        // many rows per kv head (Q K^T and P V are dense 16-row tiles), or a
-        // head shape only the matrix-core kernel's padded tiles hold
-        pl.path = MXFA_PATH_MFMA;
-        pl.row_block = mfma_row_block(p.dk(), p.dv());
-        if (odd || (MXFA_MFMA_SMALL && R <= kMfmaSmallRows && p.dk() <= 128 && p.dv() <= 128))
-            pl.row_block = kMfmaSmallRows;
-        pl.layout = kTokens;
-        // two kv heads per workgroup (two waves each) when Hkv is even and
-        // one row block holds all rows (decode): the workgroup then reads 512
-        // contiguous bytes of every token row instead of 256.  With several
-        // row blocks (prefill chunks) every block reads its head's K/V again
-        // from the caches, and pairing heads doubles what those re-reads
-        // cycle through: a packed chunked-prefill batch fell from 536 to 313
-        // TFLOP/s with pairs, so such problems keep one head per workgroup.
-        if (!odd && p.Hkv % kMfmaHeads == 0 && R <= pl.row_block) hpb = kMfmaHeads;
-    } else {
-        pl.path = MXFA_PATH_VALU;
-        pl.row_block = next_pow2_le8((int)R);
-        pl.layout = valu_layout(p.Hkv, p.D, cache_bytes < kValuStreamBytes, &hpb);
-    }
     const int row_blocks = R > 0 ? ceil_div(R, pl.row_block) : 1;
     pl.head_block = hpb;
     const int head_blocks = ceil_div(p.Hkv, hpb);
@@ -314,6 +279,87 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
     f.head_blocks = head_blocks;
     f.row_blocks = row_blocks;
     f.min_share = min_share;
+    // workgroups with work, at most (every sequence at full length)
+    if (pl.schedule == kBalanced) {
+        const long long T = streams * p.kv_cap;
+        long long W = (T + pl.grid_x - 1) / pl.grid_x;
+        if (W < min_share) W = min_share;
+        const long long nb = (T + W - 1) / W;
+        *busy = nb < pl.grid_x ? nb : pl.grid_x;
+    } else {
+        *busy = streams * S;
+    }
+    *fp = f;
+    return MXFA_OK;
+}
+
+mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *fp) {
+    mxfa_plan_t pl;
+    std::memset(&pl, 0, sizeof(pl));
+    if (num_cus <= 0) num_cus = kDefaultCUs;
+    const int G = p.Hq / p.Hkv;
+    const long long R = (long long)G * p.qLen;
+    if (R > INT32_MAX) return MXFA_ERR_UNSUPPORTED;
+    pl.rows = (int)R;
+    int hpb = 1;
+    const bool valu_dims = p.dk() == p.dv() && (p.dk() == 64 || p.dk() == 128);
+    const int mfma_min = p.dk() == 128 ? kMfmaMinRows128 : kMfmaMinRows;
+    // at exactly the 128-dim threshold, large caches (contiguous or paged)
+    // stream faster through the VALU kernel (launch.h records the crossover)
+    const uint64_t cache_bytes =
+        (uint64_t)p.B * (uint64_t)p.kv_cap * p.Hkv * (uint64_t)(p.dk() + p.dv()) * 2;
+    const bool valu_stream = p.dk() == 128 && R == kMfmaMinRows128 &&
+                             cache_bytes >= kValuStreamBytes;
+    // head dims that are not multiples of 8: 2-byte aligned rows, element
+    // loads on the matrix-core kernel's 16-row tiles, one kv head per workgroup
+    const bool odd = odd_head_dims(p.dk(), p.dv());
+    if ((R >= mfma_min && !valu_stream) || !valu_dims) {
+        // many rows per kv head (Q K^T and P V are dense 16-row tiles), or a
+        // head shape only the matrix-core kernel's padded tiles hold
+        pl.path = MXFA_PATH_MFMA;
+        pl.row_block = mfma_row_block(p.dk(), p.dv());
+        if (odd || (MXFA_MFMA_SMALL && R <= kMfmaSmallRows && p.dk() <= 128 && p.dv() <= 128))
+            pl.row_block = kMfmaSmallRows;
+        pl.layout = kTokens;
+        // two kv heads per workgroup (two waves each) when Hkv is even and
+        // one row block holds all rows (decode): the workgroup then reads 512
+        // contiguous bytes of every token row instead of 256.  With several
+        // row blocks (prefill chunks) every block reads its head's K/V again
+        // from the caches, and pairing heads doubles what those re-reads
+        // cycle through: a packed chunked-prefill batch fell from 536 to 313
+        // TFLOP/s with pairs, so such problems keep one head per workgroup.
+        if (!odd && p.Hkv % kMfmaHeads == 0 && R <= pl.row_block) hpb = kMfmaHeads;
+    } else {
+        pl.path = MXFA_PATH_VALU;
+        pl.row_block = next_pow2_le8((int)R);
+        pl.layout = valu_layout(p.Hkv, p.D, cache_bytes < kValuStreamBytes, &hpb);
+    }
+    FullPlan f;
+    long long busy = 0;
+    const mxfa_status st = finish_plan(p, R, odd, num_splits, num_cus, pl, hpb, &f, &busy);
+    if (st != MXFA_OK) return st;
+    // Many rows per kv head but few workgroups with work on 64-row tiles
+    // (short caches, few sequences or kv heads): 16-row tiles, one kv head
+    // per workgroup and two workgroups per CU give four times the row
+    // blocks, each re-reading its head's K/V, which on such caches come back
+    // from the caches rather than HBM.  Measured against the 64-row plan
+    // (bf16, causal drafts of 8 tokens, whole calls): GQA 8 with 2-4
+    // sequences at 256-2048 keys 8.1-20.9 against 16.5-39.3 us, one sequence
+    // at 8192 keys 23.6 against 30.2 us, the 128-key tiny causal batch 4.4
+    // against 6.9 us; equal where the 64-row plan keeps half the CUs busy
+    // (4 sequences at 4096 keys, 31.6 us each), and slower past it (4
+    // sequences at 8192 keys: 55.7 against 37.1 us; the 32K-key Llama-70B
+    // MTP batch keeps every CU busy on 64-row tiles).  A forced partition
+    // count keeps the tile the head shape selects.
+    if (pl.path == MXFA_PATH_MFMA && num_splits == 0 && !odd && MXFA_MFMA_SMALL &&
+        pl.row_block != kMfmaSmallRows && R > kMfmaSmallRows && p.dk() <= 128 &&
+        p.dv() <= 128 && 2 * busy <= num_cus) {
+        mxfa_plan_t p16 = pl;
+        p16.row_block = kMfmaSmallRows;
+        FullPlan f16;
+        long long busy16 = 0;
+        if (finish_plan(p, R, odd, num_splits, num_cus, p16, 1, &f16, &busy16) == MXFA_OK) f = f16;
+    }
     *fp = f;
     return MXFA_OK;
 }

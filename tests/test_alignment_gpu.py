@@ -64,9 +64,13 @@ CONTIGUOUS = [
     ("valu_d64", wl.Workload("al3", B=3, qLen=2, Hq=16, Hkv=8, D=64, kv_cap=1500,
                              dtype="bf16", causal=True, sigma=1.0, seed=73,
                              len_range=(0, 1500)), "valu", None, None),
-    ("mfma64", wl.Workload("al4", B=2, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=3000,
+    ("mfma64", wl.Workload("al4", B=16, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=1100,
                            dtype="bf16", causal=True, sigma=0.5, seed=74,
-                           len_range=(1, 3000)), "mfma", 64, 2),
+                           len_range=(1, 1100)), "mfma", 64, 2),
+    # the same draft on a short cache for two sequences: 16-row blocks
+    ("mfma16_rowblocks", wl.Workload("al4s", B=2, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=3000,
+                                     dtype="bf16", causal=True, sigma=0.5, seed=78,
+                                     len_range=(1, 3000)), "mfma", 16, 1),
     ("mfma16", wl.Workload("al5", B=1, qLen=8, Hq=16, Hkv=16, D=128, kv_cap=2000,
                            dtype="fp16", causal=False, sigma=1.0, seed=75,
                            len_range=(2000, 2000)), "mfma", 16, 2),
@@ -96,6 +100,8 @@ def test_offset_buffers_contiguous(name, w, path, rb, hb, forced):
     assert plan["path"] == path, plan
     if rb is not None and not forced:
         assert plan["row_block"] == rb and plan["head_block"] == hb, plan
+    if forced and path == "mfma" and plan["rows"] > 16 and w.D % 8 == 0:
+        assert plan["row_block"] == 64, plan     # forced partitions keep the 64-row tile
     keep = []
     views = {}
     for key, t in (("q", inp.q), ("k", inp.k_cache), ("v", inp.v_cache)):
@@ -145,9 +151,9 @@ def test_offset_buffers_separate_dims(Dk, Dv, qLen):
 
 
 PAGED = [
-    ("paged16_mfma64", wl.Workload("alp1", B=2, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=4096,
+    ("paged16_mfma64", wl.Workload("alp1", B=16, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=1104,
                                    dtype="bf16", causal=True, sigma=0.5, seed=81,
-                                   len_range=(1, 4096)), 16, "mfma", 64),
+                                   len_range=(1, 1104)), 16, "mfma", 64),
     ("paged64_valu", wl.Workload("alp2", B=4, qLen=1, Hq=16, Hkv=8, D=128, kv_cap=2048,
                                  dtype="fp16", causal=False, sigma=1.0, seed=82,
                                  len_range=(0, 2048)), 64, "valu", 2),

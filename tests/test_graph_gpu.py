@@ -31,8 +31,12 @@ CASES = [
     ("valu", wl.Workload("gv", B=8, qLen=1, Hq=32, Hkv=8, D=128, kv_cap=8192, dtype="bf16",
                          causal=False, sigma=1.0, seed=901, len_range=(0, 8192))),
     # a causal draft on the 64-row matrix-core kernel with its merge kernel
-    ("mfma64", wl.Workload("gm", B=3, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=3000, dtype="bf16",
-                           causal=True, sigma=0.5, seed=902, len_range=(0, 3000))),
+    ("mfma64", wl.Workload("gm", B=16, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=1100, dtype="bf16",
+                           causal=True, sigma=0.5, seed=902, len_range=(0, 1100))),
+    # the same draft on a short cache for three sequences: 16-row blocks
+    ("mfma16rows", wl.Workload("gr", B=3, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=3000,
+                               dtype="bf16", causal=True, sigma=0.5, seed=904,
+                               len_range=(0, 3000))),
     # the 16-row matrix-core variant, fp16
     ("mfma16", wl.Workload("gs", B=2, qLen=1, Hq=64, Hkv=8, D=128, kv_cap=2000, dtype="fp16",
                            causal=False, sigma=1.0, seed=903, len_range=(0, 2000))),
@@ -73,6 +77,8 @@ def test_captured_call_replays(kind, w, noalloc):
         call()
     plan = mx.last_plan().as_dict()
     assert plan["schedule"] == 1, plan
+    want_rb = {"valu": 4, "mfma64": 64, "mfma16rows": 16, "mfma16": 16}[kind]
+    assert plan["row_block"] == want_rb, plan
     for rep in range(4):
         # new queries and lengths in the captured tensors (eager work between replays)
         g2 = torch.Generator().manual_seed(w.seed + 100 + rep)

@@ -31,8 +31,8 @@ def _gpu():
 
 WORKLOADS = [
     # the 64-row matrix-core kernel with its merge
-    wl.Workload("st1", B=3, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=3000, dtype="bf16",
-                causal=True, sigma=0.5, seed=111, len_range=(1, 3000)),
+    wl.Workload("st1", B=16, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=1100, dtype="bf16",
+                causal=True, sigma=0.5, seed=111, len_range=(1, 1100)),
     # the vector-ALU kernel, 4 heads per workgroup
     wl.Workload("st2", B=2, qLen=1, Hq=32, Hkv=32, D=128, kv_cap=2500, dtype="fp16",
                 causal=False, sigma=1.0, seed=112, len_range=(0, 2500)),

@@ -20,7 +20,8 @@ CASES = [
     # (name, B, qLen, Hq, Hkv, D, kv_cap, dtype, causal) -> layout the planner picks
     ("aligned_valu_mha_q1", 1, 1, 32, 32, 128, 1023, "bf16", False),      # 32 shares/stream
     ("aligned_mfma16_gqa4_q2", 3, 2, 16, 4, 128, 777, "fp16", True),     # 13 shares/stream
-    ("aligned_mfma64_mtp8", 2, 8, 64, 8, 128, 5000, "bf16", True),       # 10 shares/stream
+    ("aligned_mfma16_mtp8", 2, 8, 64, 8, 128, 5000, "bf16", True),       # 16-row blocks, 8 shares/stream
+    ("aligned_mfma64_mtp8", 16, 8, 64, 8, 128, 1100, "bf16", True),      # 64-row tiles, 3 shares/stream
     ("aligned_mfma16_mha_q8_d64", 1, 8, 16, 16, 64, 3000, "fp16", True), # 47 shares/stream
     ("aligned_d96", 7, 3, 12, 4, 96, 1337, "bf16", True),                # 14 shares/stream
     ("one_share_per_stream", 256, 1, 8, 8, 64, 1000, "fp16", False),     # 256 streams, 256 shares
