@@ -57,7 +57,9 @@
 //
 // Few rows.  With at most 16 query rows per kv head (SMALL) a wave holds one
 // row tile and one LDS stage, about 215 registers and 73 KB of LDS per
-// workgroup, so two workgroups share a CU.
+// workgroup, so two workgroups share a CU.  With 17 to 32 rows a wave holds
+// two row tiles (RTO = 2) and the launch keeps one workgroup per CU, so no
+// matrix product or exponential is spent on the padded rows of a 64-row tile.
 //
 // Head dims.  The tile widths DK x DV (64 x 64, 128 x 128, 192 x 128 or
 // 256 x 256) hold any head dims Dk <= DK, Dv <= DV that are multiples of 8:
@@ -160,8 +162,10 @@ __device__ __forceinline__ u32x4 load_chunk_elems(__amdgpu_buffer_rsrc_t r, uint
 // launches; it matters most when several row blocks of a head re-read its
 // K/V from the caches, where the LDS round trip limits the kernel).
 // ODD: head dims that are not multiples of 8 (with SMALL, without KD).
+// RTO: 16-row tiles per wave when not the tile widths' default (2 for 17-32
+// rows per kv head; 0 keeps the default).
 template <int DT, int DK, int DV, int HPW, bool PAGED, int POL = MXFA_KV_LOAD_POLICY,
-          bool SMALL = false, bool KD = false, bool ODD = false>
+          bool SMALL = false, bool KD = false, bool ODD = false, int RTO = 0>
 struct Mfma {
     using T = MfmaType<DT>;
     typedef typename T::vec vec;
@@ -175,7 +179,7 @@ struct Mfma {
     static constexpr int VTB = kKT * ROWV;
     static constexpr int LDK = kKT * NCHK / 64;   // K loads per lane per tile
     static constexpr int LDV = kKT * NCHV / 64;   // V loads per lane per tile
-    static constexpr int RT = SMALL ? 1 : MfmaShape<DK, DV>::RT;          // 16-row tiles per wave
+    static constexpr int RT = SMALL ? 1 : RTO ? RTO : MfmaShape<DK, DV>::RT;   // 16-row tiles per wave
     static constexpr int STG = SMALL ? 1 : MfmaShape<DK, DV>::kStages;    // LDS tile stages per wave
     static constexpr int RB = RT * 16;            // query rows per workgroup and head
     static constexpr int WPH = kMWaves / HPW;     // waves per kv head
@@ -652,11 +656,11 @@ struct Mfma {
 // of accumulators and one K/V tile in registers.
 
 template <int DT, int DK, int DV, int HPW, int SCHED, bool PAGED, int POL, bool SMALL, bool KD,
-          bool ODD = false>
+          bool ODD = false, int RTO = 0>
 __global__ __launch_bounds__(kMWaves * 64)
 __attribute__((amdgpu_waves_per_eu(SMALL && !ODD ? 2 : 1, SMALL && !ODD ? 2 : 1)))
 void split_kv_mfma_kernel(KernelArgs a) {
-    using M = Mfma<DT, DK, DV, HPW, PAGED, POL, SMALL, KD, ODD>;
+    using M = Mfma<DT, DK, DV, HPW, PAGED, POL, SMALL, KD, ODD, RTO>;
     __shared__ __attribute__((aligned(16))) typename M::Smem sm;
     // a paged cache is read in page-aligned tiles, so its segments start on
     // tile boundaries (no key of a segment's first tile precedes it)
@@ -667,14 +671,14 @@ void split_kv_mfma_kernel(KernelArgs a) {
 }
 
 template <int DT, int DK, int DV, int HPW, int POL, bool SMALL = false, bool KD = false,
-          bool ODD = false>
+          bool ODD = false, int RTO = 0>
 const void *kernel_for(const KernelArgs &a) {
     const bool paged = a.block_table != nullptr;
     return a.schedule == kBalanced
-               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true, POL, SMALL, KD, ODD>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false, POL, SMALL, KD, ODD>)
-               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true, POL, SMALL, KD, ODD>
-                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false, POL, SMALL, KD, ODD>);
+               ? (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, true, POL, SMALL, KD, ODD, RTO>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kBalanced, false, POL, SMALL, KD, ODD, RTO>)
+               : (paged ? (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, true, POL, SMALL, KD, ODD, RTO>
+                        : (const void *)&split_kv_mfma_kernel<DT, DK, DV, HPW, kFixed, false, POL, SMALL, KD, ODD, RTO>);
 }
 
 // Head dims that are not multiples of 8: 16-row tiles, one kv head per
@@ -699,7 +703,8 @@ template <int DT, int DK, int DV>
 hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
     constexpr bool kHasSmall = DK + DV <= 256;
     const bool small = kHasSmall && a.row_block == kMfmaSmallRows;
-    if ((!small && a.row_block != Mfma<DT, DK, DV, 1, false>::RB) || a.Dk > DK || a.Dv > DV ||
+    const bool mid = kHasSmall && a.row_block == kMfmaMidRows;
+    if ((!small && !mid && a.row_block != Mfma<DT, DK, DV, 1, false>::RB) || a.Dk > DK || a.Dv > DV ||
         (a.head_block != 1 && a.head_block != 2) || a.Hkv % a.head_block != 0)
         return hipErrorInvalidValue;
     KernelArgs args = a;
@@ -708,6 +713,12 @@ hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
         if (small) {
             const void *f = a.head_block == 2 ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY, true>(a)
                                               : kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY, true>(a);
+            return hipLaunchKernel(f, grid, dim3(kMWaves * 64), kargs, 0, stream);
+        }
+        if (mid) {
+            const void *f = a.head_block == 2
+                                ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY, false, true, false, 2>(a)
+                                : kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY, false, true, false, 2>(a);
             return hipLaunchKernel(f, grid, dim3(kMWaves * 64), kargs, 0, stream);
         }
     }
