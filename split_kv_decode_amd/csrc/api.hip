@@ -320,8 +320,8 @@ mxfa_status make_plan(const Problem &p, int num_splits, int num_cus, FullPlan *f
         pl.row_block = mfma_row_block(p.dk(), p.dv());
         if (odd || (MXFA_MFMA_SMALL && R <= kMfmaSmallRows && p.dk() <= 128 && p.dv() <= 128))
             pl.row_block = kMfmaSmallRows;
-        else if (R <= kMfmaMidRows && p.dk() <= 128 && p.dv() <= 128)
-            pl.row_block = kMfmaMidRows;
+        else if (R <= kMfmaMaxMidRows && p.dk() <= 128 && p.dv() <= 128)
+            pl.row_block = (int)((R + kMfmaSmallRows - 1) / kMfmaSmallRows) * kMfmaSmallRows;
         pl.layout = kTokens;
         // two kv heads per workgroup (two waves each) when Hkv is even and
         // one row block holds all rows (decode): the workgroup then reads 512

@@ -207,15 +207,17 @@ constexpr unsigned long long kValuStreamBytes = 256ull << 20;
 #define MXFA_MFMA_SMALL 1
 #endif
 constexpr int kMfmaSmallRows = 16;
-// 17 to 32 rows per kv head (GQA 8 with 3-4 token drafts, GQA 4 with 5-8):
-// two 16-row tiles per wave, one workgroup per CU, where the 64-row tile
-// would compute as many padded rows as real ones.  Measured against the
-// 64-row tile on batches that keep every CU busy (bf16, causal, whole
-// calls): 4 x 32768 keys at 32 rows 92.7 -> 90.7 us, 1 x 32768 34.8 ->
-// 32.8, 16 x 8192 95.3 -> 93.4, 8 x 16384 at 16 query heads x 2 tokens
-// 92.4 -> 90.5, at 24 rows 91.7 -> 90.1.  (Two 32-row workgroups per CU
-// spilled at the 256-register limit and ran 9% slower.)
-constexpr int kMfmaMidRows = 32;
+// 17 to 48 rows per kv head (GQA 8 with 3-6 token drafts, GQA 16 with 2-3):
+// blocks of 32 or 48 rows, two or three 16-row tiles per wave, one
+// workgroup per CU, where the 64-row tile would compute padded rows.
+// Measured against the 64-row tile on batches that keep every CU busy
+// (bf16, causal, whole calls): at 32 rows 4 x 32768 keys 92.7 -> 90.7 us,
+// 1 x 32768 34.8 -> 32.8, 16 x 8192 95.3 -> 93.4, 8 x 16384 (16 query heads
+// x 2 tokens) 92.4 -> 90.5; at 24 rows 91.7 -> 90.1; at 48 rows 4 x 32768
+// 93.6 -> 92.7, 1 x 32768 36.0 -> 35.3, 8 x 16384 94.0 -> 93.0, head dim 64
+// 55.5 -> 54.6; at 40 rows 16 x 8192 96.5 -> 95.5.  (Two 32-row workgroups
+// per CU spilled at the 256-register limit and ran 9% slower.)
+constexpr int kMfmaMaxMidRows = 48;
 // kv heads per workgroup of the matrix-core kernel (1 or 2).  Measured on the
 // Llama-70B-shaped MTP batch (537 MB of K/V): 2 heads take the split kernel
 // from 97.6 to 93.5 us and the whole call from 101.6 to 100.0 us (the merge

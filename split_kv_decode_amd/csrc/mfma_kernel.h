@@ -57,9 +57,10 @@
 //
 // Few rows.  With at most 16 query rows per kv head (SMALL) a wave holds one
 // row tile and one LDS stage, about 215 registers and 73 KB of LDS per
-// workgroup, so two workgroups share a CU.  With 17 to 32 rows a wave holds
-// two row tiles (RTO = 2) and the launch keeps one workgroup per CU, so no
-// matrix product or exponential is spent on the padded rows of a 64-row tile.
+// workgroup, so two workgroups share a CU.  With 17 to 48 rows a wave holds
+// two or three row tiles (RTO = 2, 3) and the launch keeps one workgroup per
+// CU, so no matrix product or exponential is spent on the padded rows of a
+// 64-row tile.
 //
 // Head dims.  The tile widths DK x DV (64 x 64, 128 x 128, 192 x 128 or
 // 256 x 256) hold any head dims Dk <= DK, Dv <= DV that are multiples of 8:
@@ -163,7 +164,7 @@ __device__ __forceinline__ u32x4 load_chunk_elems(__amdgpu_buffer_rsrc_t r, uint
 // K/V from the caches, where the LDS round trip limits the kernel).
 // ODD: head dims that are not multiples of 8 (with SMALL, without KD).
 // RTO: 16-row tiles per wave when not the tile widths' default (2 for 17-32
-// rows per kv head; 0 keeps the default).
+// rows per kv head, 3 for 33-48; 0 keeps the default).
 template <int DT, int DK, int DV, int HPW, bool PAGED, int POL = MXFA_KV_LOAD_POLICY,
           bool SMALL = false, bool KD = false, bool ODD = false, int RTO = 0>
 struct Mfma {
@@ -703,7 +704,8 @@ template <int DT, int DK, int DV>
 hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
     constexpr bool kHasSmall = DK + DV <= 256;
     const bool small = kHasSmall && a.row_block == kMfmaSmallRows;
-    const bool mid = kHasSmall && a.row_block == kMfmaMidRows;
+    // 32- and 48-row blocks: two or three 16-row tiles per wave
+    const bool mid = kHasSmall && (a.row_block == 2 * kMfmaSmallRows || a.row_block == 3 * kMfmaSmallRows);
     if ((!small && !mid && a.row_block != Mfma<DT, DK, DV, 1, false>::RB) || a.Dk > DK || a.Dv > DV ||
         (a.head_block != 1 && a.head_block != 2) || a.Hkv % a.head_block != 0)
         return hipErrorInvalidValue;
@@ -716,9 +718,13 @@ hipError_t launch_t(const KernelArgs &a, dim3 grid, hipStream_t stream) {
             return hipLaunchKernel(f, grid, dim3(kMWaves * 64), kargs, 0, stream);
         }
         if (mid) {
-            const void *f = a.head_block == 2
-                                ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY, false, true, false, 2>(a)
-                                : kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY, false, true, false, 2>(a);
+            const bool three = a.row_block == 3 * kMfmaSmallRows;
+            const void *f =
+                a.head_block == 2
+                    ? (three ? kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY, false, true, false, 3>(a)
+                             : kernel_for<DT, DK, DV, 2, MXFA_KV_LOAD_POLICY, false, true, false, 2>(a))
+                    : (three ? kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY, false, true, false, 3>(a)
+                             : kernel_for<DT, DK, DV, 1, MXFA_KV_LOAD_POLICY, false, true, false, 2>(a));
             return hipLaunchKernel(f, grid, dim3(kMWaves * 64), kargs, 0, stream);
         }
     }

@@ -272,10 +272,11 @@ def test_plan_routes_head_dims():
     for D, rb in ((96, 64), (256, 16), (200, 16)):
         p = m.plan(4, 64, 2, D, 2, 4096, 0, 1, 3)                # 64 rows per kv head
         assert p.path == 1 and p.row_block == rb, D
-    for D, rb in ((96, 32), (128, 32), (64, 32), (256, 16)):
-        p = m.plan(4, 32, 2, D, 2, 4096, 0, 1, 3)                # 32 rows per kv head
-        assert p.path == 1 and p.row_block == rb, D
-        assert p.head_block == (2 if rb == 32 else 1), D
+    for rows, D, rb in ((32, 96, 32), (32, 128, 32), (32, 64, 32), (32, 256, 16),
+                        (48, 128, 48), (40, 64, 48), (34, 96, 48), (48, 200, 16)):
+        p = m.plan(4, rows // 2 * 2, 2, D, 2, 4096, 0, 1, 3)      # rows per kv head
+        assert p.path == 1 and p.row_block == rb and p.rows == rows, (rows, D)
+        assert p.head_block == (2 if rb in (32, 48) else 1), (rows, D)
     # head dims that are not multiples of 8: 16-row tiles, one kv head per
     # workgroup, one workgroup per CU in the balanced grid
     for D in (1, 3, 17, 36, 100, 129, 130, 255):
@@ -311,7 +312,9 @@ def test_plan_takes_16_row_tiles_when_64_row_tiles_leave_cus_idle():
             assert p.head_block == 1 and p.schedule in (0, 1)
         # a forced partition count keeps the tile the head shape selects
         f = m.plan(B, Hq, Hkv, D, qLen, cap, 1, 1, 3, 256)
-        assert f.row_block == (32 if qLen * Hq // Hkv <= 32 else 64) and f.schedule == 0, \
+        rows = qLen * Hq // Hkv
+        assert f.row_block == (32 if rows <= 32 else 48 if rows <= 48 else 64) and \
+            f.schedule == 0, \
             (B, qLen, Hq, Hkv, D, cap)
     # the rule counts CUs: the same 4 x 4096 batch fills half of 128 CUs
     assert m.plan(4, 64, 8, 128, 8, 4096, 1, 1, 0, 128).row_block == 64
@@ -394,18 +397,18 @@ def check_plan(B, Hq, Hkv, D, qLen, cap, causal, dt, num_splits, cus=0):
         # not a multiple of 8: 16-row tiles, one kv head per workgroup
         assert p.path == 1 and p.row_block == 16 and p.head_block == 1
     elif D not in (64, 128) or (p.rows >= (4 if D == 128 else 8) and not valu_stream):
-        # matrix-core kernel: 16-row blocks up to 16 rows, 32 up to 32, else
-        # 64 (other dims pad to tiles of 64, 128 or 256 channels; 16 rows at
-        # 256); two kv heads per workgroup when Hkv is even and one block
-        # holds every row.  With more than 16 rows the planner may still take
+        # matrix-core kernel: 16-row blocks up to 16 rows, 32 up to 32, 48 up
+        # to 48, else 64 (other dims pad to tiles of 64, 128 or 256 channels;
+        # 16 rows at 256); two kv heads per workgroup when Hkv is even and one
+        # block holds every row.  With more than 16 rows the planner may still take
         # 16-row tiles when its first choice would leave most CUs without
         # work (its own partition count only; then one kv head per workgroup)
         tile = 64 if D <= 64 else 128 if D <= 128 else 256
         rb = (16 if (p.rows <= 16 and tile <= 128) or tile == 256
-              else 32 if p.rows <= 32 else 64)
+              else 32 if p.rows <= 32 else 48 if p.rows <= 48 else 64)
         pair = Hkv % 2 == 0 and p.rows <= rb
         assert p.path == 1
-        if rb in (32, 64) and p.row_block == 16:
+        if rb in (32, 48, 64) and p.row_block == 16:
             assert num_splits == 0 and p.head_block == 1 and tile <= 128
         else:
             assert p.row_block == rb and p.head_block == (2 if pair else 1)

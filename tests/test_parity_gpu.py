@@ -133,13 +133,15 @@ def test_matrix_core_many_rows_keep_one_head_per_workgroup(num_splits, rb):
     assert plan["row_block"] == rb, plan
 
 
-@pytest.mark.parametrize("num_splits,rb", [(2, 64), (0, 16)])
+@pytest.mark.parametrize("num_splits", [2, 0])
 @pytest.mark.parametrize("Hkv,qLen", [(3, 8), (3, 5), (5, 6)])
-def test_matrix_core_one_block_one_head(Hkv, qLen, num_splits, rb):
-    """One 64-row block per kv head with an odd Hkv: one kv head per
-    workgroup, K loaded straight into the operand layout, ragged lengths and
-    a causal draft (forced partitions); with the planner's own partitions
-    this short cache takes 16-row blocks instead."""
+def test_matrix_core_one_block_one_head(Hkv, qLen, num_splits):
+    """One block per kv head (64 rows, or 48 for 40-48 rows) with an odd Hkv:
+    one kv head per workgroup, K loaded straight into the operand layout,
+    ragged lengths and a causal draft (forced partitions); with the
+    planner's own partitions this short cache takes 16-row blocks instead."""
+    R = 8 * qLen
+    rb = 16 if num_splits == 0 else (48 if R <= 48 else 64)
     w = wl.Workload("onehead", B=3, qLen=qLen, Hq=8 * Hkv, Hkv=Hkv, D=128, kv_cap=800,
                     dtype="bf16", causal=True, sigma=1.0, seed=960 + Hkv + qLen,
                     len_range=(1, 800))

@@ -5,8 +5,8 @@ and 64 or 128 query heads; 16, 24 or 32 query heads per kv head), where a kv
 head carries up to 512 query rows, split into several 64-row blocks with a
 ragged last block, or fit one 16-row tile; and batches on both sides of the
 1024-sequence limit of the balanced schedule (more sequences take fixed
-partitions); and the 32-row tiles (two 16-row tiles per wave) that 17 to
-32 rows per kv head take.  Every row is compared with the fp64 oracle.
+partitions); and the 32- and 48-row tiles (two or three 16-row tiles per
+wave) that 17 to 48 rows per kv head take.  Every row is compared with the fp64 oracle.
 """
 import pytest
 import torch
@@ -70,16 +70,21 @@ def test_batches_around_the_balanced_limit(B, schedule, qLen, Hq, Hkv, cap):
 
 
 MID_PLANNED = [
-    # 17-32 rows per kv head on batches that keep every CU busy: the planner's
-    # balanced schedule on two 16-row tiles per wave
-    ("gqa16_q4", 16, 4, 64, 8, 128, 2048, "bf16", True),
-    ("gqa16_q2", 4, 2, 128, 8, 128, 3000, "fp16", True),
+    # 17-48 rows per kv head on batches that keep every CU busy: the planner's
+    # balanced schedule on two or three 16-row tiles per wave
+    ("gqa8_q4", 16, 4, 64, 8, 128, 2048, "bf16", True),          # 32 rows
+    ("gqa16_q2", 4, 2, 128, 8, 128, 3000, "fp16", True),         # 32 rows
+    ("gqa8_q6", 16, 6, 64, 8, 128, 2048, "bf16", True),          # 48 rows
+    ("gqa16_q3", 8, 3, 128, 8, 128, 2500, "fp16", True),         # 48 rows
 ]
 MID_FORCED = [
     # small caches (the planner would take 16-row blocks): forced partitions
     ("gqa8_q3_even_kv", 3, 3, 48, 6, 128, 500, "fp16", True),     # 24 rows, two heads per workgroup
     ("gqa8_q4_odd_kv_d64", 2, 4, 24, 3, 64, 900, "bf16", True),   # 32 rows, one head, head dim 64
     ("mha_q17", 1, 17, 8, 8, 128, 300, "fp16", False),             # 17 rows
+    ("gqa8_q5_even_kv", 3, 5, 48, 6, 128, 500, "bf16", True),     # 40 rows in a 48-row block
+    ("gqa8_q6_odd_kv_d64", 2, 6, 24, 3, 64, 900, "fp16", True),   # 48 rows, one head, head dim 64
+    ("mha_q33", 1, 33, 8, 8, 128, 300, "bf16", False),             # 33 rows
 ]
 
 
@@ -89,20 +94,25 @@ def _mid_workload(case):
                        causal=causal, sigma=1.0, seed=B + qLen + D, len_range=(0, cap))
 
 
+def _mid_rows(w):
+    R = w.Hq // w.Hkv * w.qLen
+    return -(-R // 16) * 16
+
+
 @pytest.mark.parametrize("case", MID_PLANNED, ids=[c[0] for c in MID_PLANNED])
-def test_32_row_tiles_planned(case):
+def test_mid_row_tiles_planned(case):
     w = _mid_workload(case)
     inp = wl.make_inputs(w)
     print(f"case {w.name}", flush=True)
     out, lse, plan = parity.run_gpu(inp)
-    assert plan["row_block"] == 32 and plan["schedule"] == 1, plan
+    assert plan["row_block"] == _mid_rows(w) and plan["schedule"] == 1, plan
     ref_o, ref_l = parity.oracle_full(inp)
     print(w.name, plan, parity.compare(out, lse, ref_o, ref_l, w.dtype), flush=True)
 
 
 @pytest.mark.parametrize("page", [0, 32])
 @pytest.mark.parametrize("case", MID_FORCED, ids=[c[0] for c in MID_FORCED])
-def test_32_row_tiles_forced_and_paged(case, page):
+def test_mid_row_tiles_forced_and_paged(case, page):
     w = _mid_workload(case)
     inp = wl.make_inputs(w)
     print(f"case {w.name} page={page}", flush=True)
@@ -113,6 +123,6 @@ def test_32_row_tiles_forced_and_paged(case, page):
     else:
         out, lse, plan = parity.run_gpu(inp, num_splits=3)
         ref_o, ref_l = parity.oracle_full(inp)
-    assert plan["row_block"] == 32 and plan["schedule"] == 0, plan
+    assert plan["row_block"] == _mid_rows(w) and plan["schedule"] == 0, plan
     assert plan["head_block"] == (2 if w.Hkv % 2 == 0 else 1), plan
     print(w.name, page, plan, parity.compare(out, lse, ref_o, ref_l, w.dtype), flush=True)
