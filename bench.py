@@ -125,7 +125,7 @@ def _kernel_rows(csv_path):
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma_dir=None,
-                       page_size=0):
+                       page_size=0, out_dir=None, traffic_file=None):
     """Turn rocprofv3 outputs (kernel-trace stats, FETCH_SIZE pass, WRITE_SIZE
     pass, each of a bench run with --copy-calibration, and for the matrix-core
     kernel a MfmaUtil / MfmaFlopsBF16 / MfmaFlopsF16 pass) into a short
@@ -133,7 +133,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma
     reports.  The traffic counters are scaled by what they read for the 1 GiB
     device copy.  With page_size P the run read a paged cache: the record is
     the workload's paged one (NAME_pagedP) and the algorithmic bytes add one
-    block-table entry per page touched."""
+    block-table entry per page touched.  out_dir / traffic_file: where the
+    summary and the record go (profiles/ and its traffic.json by default).
+    Returns the record."""
     import statistics
     stats = _kernel_rows(os.path.join(trace_dir, "run_kernel_stats.csv"))
     fetch = _kernel_rows(os.path.join(fetch_dir, "run_counter_collection.csv"))
@@ -218,12 +220,14 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma
                   f"- algorithmic flops / trace average / 2.5 PFLOP/s: "
                   f"{100 * alg_fl / (avg_ns * 1e-9) / 2.5e15:.2f}%"]
         mfma_rec = {"mfma_util_pct": util, "mfma_flops": fl, "algorithmic_flops": alg_fl}
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    path = os.path.join(ROOT, "profiles", f"{kname}_{workload}.md")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    traffic_file = traffic_file or TRAFFIC_FILE
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, f"{kname}_{workload}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         rec = {}
@@ -233,9 +237,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma
                      "fetch_raw_kib": round(f_raw / 1024, 1), "write_raw_kib": round(w_raw / 1024, 1),
                      "mfma": mfma_rec,
                      "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(path)
+    return rec[workload]
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0

@@ -1,6 +1,11 @@
 """Host logic of bench.py that needs no GPU: the source digest that keeps the
-recorded counter traffic tied to the code it was measured on."""
+recorded counter traffic tied to the code it was measured on, the profile
+summary's counter arithmetic, and the one-GPU guard."""
+import os
+
 import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 SRC = """// a line comment
@@ -58,3 +63,60 @@ def test_library_binds_to_the_hip_runtime_torch_brings():
     import torch
     torch_lib = os.path.join(os.path.dirname(torch.__file__), "lib")
     assert len(paths) == 1 and paths[0].startswith(torch_lib), paths
+
+
+def _csv(path, header, rows):
+    import csv
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_profile_summary_scales_the_counters_by_the_copy_calibration(tmp_path):
+    """The traffic record is the split kernel's median FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) times what a 1 GiB device copy reads as,
+    and the achieved rate is the algorithmic bytes over the trace average."""
+    import json
+    import bench
+    import workloads as wl
+    split = "void mxfa::split_kv_valu_kernel<0, 128, 4, 4, 1, 1, false>(mxfa::KernelArgs)"
+    merge = "void mxfa::combine_kernel<0, 128, 4, false>(mxfa::KernelArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    _csv(tmp_path / "t" / "run_kernel_stats.csv", ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
+         [[split, 65, 10000.0, 9000, 12000], [merge, 65, 4000.0, 3500, 5000]])
+    gib_kib = (1 << 30) // 1024
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    fetch = [[copy, "FETCH_SIZE", gib_kib // 2]] * 3 + \
+        [[split, "FETCH_SIZE", v] for v in (30000, 31000, 32000, 33000, 34000)] + \
+        [[merge, "FETCH_SIZE", 300]] * 5
+    write = [[copy, "WRITE_SIZE", gib_kib]] * 3 + \
+        [[split, "WRITE_SIZE", v] for v in (500, 510, 520, 530, 540)] + [[merge, "WRITE_SIZE", 8]] * 5
+    _csv(tmp_path / "f" / "run_counter_collection.csv", hdr, fetch)
+    _csv(tmp_path / "w" / "run_counter_collection.csv", hdr, write)
+    traffic = tmp_path / "traffic.json"
+    rec = bench.summarize_profiles(str(tmp_path / "t"), str(tmp_path / "f"), str(tmp_path / "w"),
+                                   "smallq_mha_q1_kv1023", ["cmd"], out_dir=str(tmp_path / "p"),
+                                   traffic_file=str(traffic))
+    # fetch reads half a copy's bytes (scale 2), write all of them (scale 1)
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["fetch_raw_kib"] == 32000 and rec["write_raw_kib"] == 520
+    assert rec["fetch_bytes"] == 32000 * 1024 * 2 and rec["write_bytes"] == 520 * 1024
+    assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
+    assert rec["kernel"] == "split_kv_valu_kernel"
+    assert rec["kernel_digest"] == bench.kernel_digest("split_kv_valu_kernel")
+    assert json.load(open(traffic))["smallq_mha_q1_kv1023"] == rec
+    text = (tmp_path / "p" / "split_kv_valu_kernel_smallq_mha_q1_kv1023.md").read_text()
+    w = wl.WORKLOADS["smallq_mha_q1_kv1023"]
+    alg = wl.kv_bytes(w, [w.kv_cap] * w.B) + w.B * w.qLen * w.Hq * w.D * w.elt
+    assert f"{alg / 10e-6 / 1e9:.1f} GB/s" in text          # over the 10 us trace average
+    assert "| 65 | 10.0 |" in text and "| 65 | 4.0 |" in text
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and not r.stdout
