@@ -162,9 +162,16 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma
     f_split, w_split = f_raw * f_scale, w_raw * w_scale
 
     import workloads as wl
-    w = wl.WORKLOADS[workload]
-    lens = wl.make_inputs(w).lengths() if w.len_range else [w.kv_cap] * w.B
-    alg = wl.kv_bytes(w, lens) + w.B * w.qLen * w.Hq * w.D * w.elt
+    packed = workload in wl.VARLEN_WORKLOADS
+    if packed:
+        # a packed batch: distinct K/V + Q bytes once; attention flops
+        w = wl.VARLEN_WORKLOADS[workload]
+        lens = list(w.klens)
+        alg = 2 * sum(w.klens) * w.Hkv * w.D * 2 + sum(w.qlens) * w.Hq * w.D * 2
+    else:
+        w = wl.WORKLOADS[workload]
+        lens = wl.make_inputs(w).lengths() if w.len_range else [w.kv_cap] * w.B
+        alg = wl.kv_bytes(w, lens) + w.B * w.qLen * w.Hq * w.D * w.elt
     if page_size:
         alg += sum(-(-max(0, min(n, w.kv_cap)) // page_size) for n in lens) * 4
         workload = f"{workload}_paged{page_size}"
@@ -195,6 +202,13 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma
               f"fetched / algorithmic = {f_split / alg:.4f}",
               f"- achieved from the trace average: {alg / (avg_ns * 1e-9) / 1e9:.1f} GB/s "
               f"({100 * alg / (avg_ns * 1e-9) / 1e9 / HBM_PEAK_GBS:.1f}% of 8 TB/s)"]
+    if packed:
+        fl_alg = wl.varlen_flops(w)
+        lines.append(f"- attention flops per launch {fl_alg / 1e9:.1f} GFLOP: "
+                     f"{fl_alg / (avg_ns * 1e-9) / 1e12:.1f} TFLOP/s from the trace average "
+                     f"({100 * fl_alg / (avg_ns * 1e-9) / 2.5e15:.1f}% of 2.5 PFLOP/s); the "
+                     f"fetched bytes are {f_split / alg:.2f}x the distinct K/V + Q bytes, "
+                     f"since every row block of a kv head reads its K/V")
     if merge:
         fmr, wmr = statistics.median(f_by[merge[0]]), statistics.median(w_by[merge[0]])
         lines.append(f"- merge kernel: raw FETCH_SIZE {fmr / 1024:.0f} KiB, WRITE_SIZE "
@@ -209,8 +223,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma
                 by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
         util = statistics.median(by["MfmaUtil"]) if "MfmaUtil" in by else None
         fl = sum(statistics.median(by[k]) for k in ("MfmaFlopsBF16", "MfmaFlopsF16") if k in by)
-        pairs = wl.visible_pairs(w, lens)
-        alg_fl = 4 * w.D * pairs
+        alg_fl = wl.varlen_flops(w) if packed else 4 * w.D * wl.visible_pairs(w, lens)
         lines += ["", "## Matrix cores (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 MfmaFlopsF16)", "",
                   f"- MfmaUtil (MFMA busy cycles / (GPU active cycles x SIMDs)): {util:.2f}%"
                   if util is not None else "- MfmaUtil: not reported",
@@ -299,6 +312,13 @@ def bench_varlen(args):
 
     ms, split_ms = time_calls(call, args.steps, args.warmup, torch, np, mx, stream)
     plan = mx.last_plan().as_dict()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     fl = wl.varlen_flops(w)
     tflops = fl / (ms * 1e-3) / 1e12
     split_tflops = fl / (split_ms * 1e-3) / 1e12
@@ -342,7 +362,8 @@ def bench_varlen(args):
         "roofline": {"bound": "mfma", "kernel": SPLIT_KERNEL[plan["path"]],
                      "achieved": round(split_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(split_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": fl,
+                     "traffic": traffic_for(w.name, SPLIT_KERNEL[plan["path"]]),
+                     "flops_per_launch": fl,
                      "mean_launch_us": round(split_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }

@@ -114,6 +114,34 @@ def test_profile_summary_scales_the_counters_by_the_copy_calibration(tmp_path):
     assert "| 65 | 10.0 |" in text and "| 65 | 4.0 |" in text
 
 
+def test_profile_summary_of_a_packed_batch(tmp_path):
+    """The packed chunked-prefill batch: the same counter arithmetic, its
+    distinct K/V + Q bytes and its attention flops."""
+    import bench
+    import workloads as wl
+    split = "void mxfa::mfma::split_kv_mfma_kernel<1, 128, 128, 1, 0, false, 0, false, true, false, 0>(mxfa::KernelArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    _csv(tmp_path / "t" / "run_kernel_stats.csv", ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
+         [[split, 25, 900000.0, 880000, 950000]])
+    gib_kib = (1 << 30) // 1024
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    _csv(tmp_path / "f" / "run_counter_collection.csv", hdr,
+         [[copy, "FETCH_SIZE", gib_kib // 2]] * 3 + [[split, "FETCH_SIZE", 1000000]] * 3)
+    _csv(tmp_path / "w" / "run_counter_collection.csv", hdr,
+         [[copy, "WRITE_SIZE", gib_kib]] * 3 + [[split, "WRITE_SIZE", 20000]] * 3)
+    rec = bench.summarize_profiles(str(tmp_path / "t"), str(tmp_path / "f"), str(tmp_path / "w"),
+                                   "llama70b_chunked_prefill", ["cmd"],
+                                   out_dir=str(tmp_path / "p"),
+                                   traffic_file=str(tmp_path / "traffic.json"))
+    assert rec["kernel"] == "split_kv_mfma_kernel" and rec["fetch_bytes"] == 1000000 * 2048
+    w = wl.VARLEN_WORKLOADS["llama70b_chunked_prefill"]
+    text = (tmp_path / "p" / "split_kv_mfma_kernel_llama70b_chunked_prefill.md").read_text()
+    fl = wl.varlen_flops(w)
+    assert f"{fl / 900e-6 / 1e12:.1f} TFLOP/s from the trace average" in text
+    alg = 2 * sum(w.klens) * w.Hkv * w.D * 2 + sum(w.qlens) * w.Hq * w.D * 2
+    assert f"{1000000 * 2048 / alg:.2f}x the distinct" in text
+
+
 def test_bench_refuses_more_than_one_gpu():
     import subprocess
     import sys
