@@ -37,6 +37,11 @@ CASES = [
     ("mfma16rows", wl.Workload("gr", B=3, qLen=8, Hq=64, Hkv=8, D=128, kv_cap=3000,
                                dtype="bf16", causal=True, sigma=0.5, seed=904,
                                len_range=(0, 3000))),
+    # 4- and 6-token drafts on GQA 8: 32- and 48-row blocks
+    ("mfma32", wl.Workload("g32", B=16, qLen=4, Hq=64, Hkv=8, D=128, kv_cap=2048, dtype="bf16",
+                           causal=True, sigma=0.5, seed=905, len_range=(0, 2048))),
+    ("mfma48", wl.Workload("g48", B=16, qLen=6, Hq=64, Hkv=8, D=128, kv_cap=2048, dtype="fp16",
+                           causal=True, sigma=0.5, seed=906, len_range=(0, 2048))),
     # the 16-row matrix-core variant, fp16
     ("mfma16", wl.Workload("gs", B=2, qLen=1, Hq=64, Hkv=8, D=128, kv_cap=2000, dtype="fp16",
                            causal=False, sigma=1.0, seed=903, len_range=(0, 2000))),
@@ -77,7 +82,8 @@ def test_captured_call_replays(kind, w, noalloc):
         call()
     plan = mx.last_plan().as_dict()
     assert plan["schedule"] == 1, plan
-    want_rb = {"valu": 4, "mfma64": 64, "mfma16rows": 16, "mfma16": 16}[kind]
+    want_rb = {"valu": 4, "mfma64": 64, "mfma16rows": 16, "mfma32": 32, "mfma48": 48,
+               "mfma16": 16}[kind]
     assert plan["row_block"] == want_rb, plan
     for rep in range(4):
         # new queries and lengths in the captured tensors (eager work between replays)
