@@ -1,6 +1,8 @@
 """Seeded random configurations on the GPU vs the fp64 oracle (needs an
 MI355X).  A second, wider draw (up to 32 kv heads, any head dim, longer
-caches) adds 200 cases.
+caches) adds 200 cases, and a third, 48 cases of grouped-query drafts with
+16 to 128 rows per kv head on batches large enough for the planner to keep
+the 32-, 48- and 64-row matrix-core tiles under either schedule.
 
 Each case draws a shape (batch, query length, GQA group, kv heads, head dim
 64 or 128, dtype, causal mask, capacity), ragged lengths including empty
@@ -194,5 +196,50 @@ def test_random_wide_configuration(case):
     else:
         out, lse, plan = parity.run_gpu(inp, num_splits)
         ref_o, ref_l = parity.oracle_full(inp)
+    rep = parity.compare(out, lse, ref_o, ref_l, w.dtype)
+    print(case, plan, rep, flush=True)
+
+
+def draw_tiles(case):
+    """GQA groups of 4-16 with 3-8 query tokens (12-128 rows per kv head), 1-8
+    kv heads, 6-24 sequences of 1000-3000 keys: the planner's 32-, 48- and
+    64-row tiles with one or two kv heads per workgroup, balanced and fixed."""
+    r = np.random.default_rng([SEED + 2, case])
+    B = int(r.integers(6, 25))
+    G = int(r.choice([4, 6, 8, 12, 16]))
+    qLen = int(r.choice([3, 4, 5, 6, 8]))
+    Hkv = int(r.choice([1, 2, 3, 4, 8]))
+    D = int(r.choice([64, 128]))
+    dtype = str(r.choice(["fp16", "bf16"]))
+    cap = int(r.integers(1000, 3001))
+    lengths = [int(x) for x in r.integers(0, cap + 1, size=B)]
+    lengths[int(r.integers(0, B))] = cap
+    if r.random() < 0.3:
+        lengths[int(r.integers(0, B))] = 0
+    num_splits = int(r.choice([0, 0, 0, 4]))
+    page = int(r.choice([0, 0, 16, 64]))
+    w = wl.Workload(f"tiles{case}", B=B, qLen=qLen, Hq=G * Hkv, Hkv=Hkv, D=D, kv_cap=cap,
+                    dtype=dtype, causal=bool(r.integers(0, 4)), sigma=float(r.choice([0.5, 1.0])),
+                    seed=SEED + 9000 + case, len_range=(0, cap))
+    return w, lengths, num_splits, page
+
+
+N_TILE_CASES = 48
+
+
+@pytest.mark.parametrize("case", range(N_TILE_CASES))
+def test_random_tile_configuration(case):
+    w, lengths, num_splits, page = draw_tiles(case)
+    inp = wl.make_inputs(w, lengths=lengths)
+    print(f"case {case}: {w.describe()} lengths={lengths} splits={num_splits} page={page}",
+          flush=True)
+    if page:
+        pg = wl.to_paged(inp, page, seed=case)
+        out, lse, plan = parity.run_gpu_paged(pg, inp, num_splits)
+        ref_o, ref_l = parity.oracle_paged(pg, inp)
+    else:
+        out, lse, plan = parity.run_gpu(inp, num_splits)
+        ref_o, ref_l = parity.oracle_full(inp)
+    assert plan["path"] == "mfma", plan
     rep = parity.compare(out, lse, ref_o, ref_l, w.dtype)
     print(case, plan, rep, flush=True)
