@@ -110,7 +110,8 @@ typedef struct {
                             1 = balanced: grid_x workgroups share the
                             concatenated KV streams of all sequences equally */
     int rows;            /* R = (Hq / Hkv) * qLen query rows per kv head */
-    int row_block;       /* query rows handled by one workgroup */
+    int row_block;       /* query rows handled by one workgroup and kv head:
+                            VALU 1, 2, 4 or 8; matrix-core 16, 32, 48 or 64 */
     int head_block;      /* kv heads handled by one workgroup */
     int num_splits;      /* fixed: KV partitions per stream at kv_cap;
                             balanced: number of workgroups */
