@@ -221,7 +221,9 @@ mxfa_status finish_plan(const Problem &p, long long R, bool odd, int num_splits,
     // on the 1023-token SmallQ cases, where the floor decides how many
     // workgroups get work: 14.3 against 17.4 us per call at q1 and 15.8
     // against 18.7 at q2 for 32 tokens against 64 (16 gained nothing more),
-    // and 16.3 against 16.7 us at q8 for 64 tokens against 128.
+    // and 16.3 against 16.7 us at q8 for 64 tokens against 128; on the
+    // final kernels 12.1 against 12.7 us at q8 for 64 tokens against 32
+    // (4 or 2 tokens per row changed no other SmallQ or small GQA call).
     constexpr int kShareAlign = 32;
     const int min_share = ceil_div(8 * rows_held > 32 ? 8 * rows_held : 32, kShareAlign) *
                           kShareAlign;
