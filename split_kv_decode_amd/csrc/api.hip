@@ -463,6 +463,11 @@ mxfa_status run(const void *q, const void *k, const void *v, const int32_t *seql
     a.chunk = pl.chunk;
     a.S = pl.num_splits;
     a.min_share = f.min_share;
+    // fixed partitions of several row blocks per kv head: head block
+    // fastest in launch order, so each XCD serves whole kv heads (when the
+    // head blocks and the 8 XCDs divide one another)
+    a.xcd_heads = pl.schedule == kFixed && f.row_blocks > 1 &&
+                  (f.head_blocks % 8 == 0 || 8 % f.head_blocks == 0);
     if (pl.schedule == kBalanced && !a.seqlens && !a.cu_k)
         uniform_shares(p.kv_cap, (long long)p.B * f.head_blocks * f.row_blocks, a.S,
                        a.min_share, &a.uni_w, &a.uni_spw);

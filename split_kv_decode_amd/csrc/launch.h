@@ -71,6 +71,9 @@ struct KernelArgs {
     // the host: tokens per workgroup share, and shares per stream when each
     // stream gets shares of its own (0: the streams are concatenated)
     int uni_w, uni_spw;
+    // kFixed with several row blocks per kv head: 1 when the workgroups are
+    // numbered head block fastest (see drive_schedule), else 0
+    int xcd_heads;
     float qscale;             // log2(e) / sqrt(D)
 };
 
