@@ -207,8 +207,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload, commands, mfma
         lines.append(f"- attention flops per launch {fl_alg / 1e9:.1f} GFLOP: "
                      f"{fl_alg / (avg_ns * 1e-9) / 1e12:.1f} TFLOP/s from the trace average "
                      f"({100 * fl_alg / (avg_ns * 1e-9) / 2.5e15:.1f}% of 2.5 PFLOP/s); the "
-                     f"fetched bytes are {f_split / alg:.2f}x the distinct K/V + Q bytes, "
-                     f"since every row block of a kv head reads its K/V")
+                     f"fetched bytes are {f_split / alg:.2f}x the distinct K/V + Q bytes "
+                     f"(every row block of a kv head reads its K/V; this counts the reads "
+                     f"that miss the L2s)")
     if merge:
         fmr, wmr = statistics.median(f_by[merge[0]]), statistics.median(w_by[merge[0]])
         lines.append(f"- merge kernel: raw FETCH_SIZE {fmr / 1024:.0f} KiB, WRITE_SIZE "
