@@ -143,7 +143,9 @@ __device__ __forceinline__ void drive_schedule(const KernelArgs &a, Segment &&se
             // all eight fetching it: 5.4 times fewer bytes fetched past the
             // L2s on the Llama-70B-shaped chunked prefill (0.35 against 1.89
             // GiB per launch, at the same speed).  Every head carries the
-            // same work, so the XCDs stay equally loaded.
+            // same work, so the XCDs stay equally loaded.  The numbering is a
+            // bijection of the grid, so results do not depend on where the
+            // workgroups run; only the cache sharing does.
             const long long L = blockIdx.x + (long long)gridDim.x *
                                                   (blockIdx.y + (long long)gridDim.y * blockIdx.z);
             const int hb = (int)(L % a.head_blocks);
