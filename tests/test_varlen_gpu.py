@@ -89,3 +89,36 @@ def test_varlen_single_sequence_equals_padded_call():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2[0])
     assert torch.equal(l1, l2[0].reshape(8, 4))
+
+
+def test_varlen_chunked_prefill_full_size_sampled():
+    """The Llama-70B-shaped chunked-prefill batch at full size (512/512/256/128
+    queries against 8K/16K/4K/32K keys, 64/8 heads): fixed partitions with 64
+    row blocks per kv head, numbered head block fastest so that each XCD
+    serves whole kv heads.  Sampled rows of every sequence (first, last and
+    random queries, every head) against the fp64 oracle, each sequence taken
+    on its own as a causal (bottom-right) problem; every output finite."""
+    import split_kv_decode_amd as mx
+    import workloads as wl
+    w = wl.VARLEN_WORKLOADS["llama70b_chunked_prefill"]
+    q, k, v, cq, ck = wl.make_varlen_inputs(w)
+    mq, mk = max(w.qlens), max(w.klens)
+    print("case llama70b_chunked_prefill full size", flush=True)
+    out, lse = mx.fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cq.cuda(), ck.cuda(), mq, mk, True)
+    torch.cuda.synchronize()
+    plan = mx.last_plan().as_dict()
+    assert plan["schedule"] == 0 and plan["row_block"] == 64 and plan["head_block"] == 1, plan
+    assert plan["grid_y"] == w.Hkv * (-(-plan["rows"] // 64)), plan
+    out64 = parity.to_f64(out)
+    lse64 = lse.cpu().double().numpy()
+    assert np.isfinite(out64).all() and np.isfinite(lse64).all()
+    r = np.random.default_rng(601)
+    for b, (ql, kl) in enumerate(zip(w.qlens, w.klens)):
+        q0, k0 = int(cq[b]), int(ck[b])
+        qs = sorted({0, ql - 1, *[int(x) for x in r.integers(0, ql, size=3)]})
+        rows = [(0, h, i) for i in qs for h in range(w.Hq)]
+        ref_o, ref_l = oracle.attention_rows(q[q0:q0 + ql].unsqueeze(0), k[k0:k0 + kl].unsqueeze(0),
+                                             v[k0:k0 + kl].unsqueeze(0), rows, None, True, w.dtype)
+        go = np.stack([out64[q0 + i, h] for (_, h, i) in rows])
+        gl = np.array([lse64[h, q0 + i] for (_, h, i) in rows])
+        print(b, ql, kl, parity.compare(go, gl, ref_o, ref_l, w.dtype), flush=True)
